@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark one step of the paged-attention hot path on one MI355X.
+
+A step is the whole path over one synthetic batch with its inputs resident in
+HBM: copy-on-write block copies, the slot-mapping write of the new tokens,
+and causal paged attention of every query row (plan, multi-token MFMA
+kernel, vector-ALU row kernel, split combine).  The default workload is the
+64-sequence fp16 decode batch at 40 heads x 128 (block size 16, contexts
+uniform in 128..2048); ``--config`` picks another named workload.
+
+Prints one JSON line.  ``value`` is whole-step throughput in GB/s of
+algorithmic bytes; ``roofline`` rates the dominant kernel from its own
+per-launch HIP events; ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "paged-attn KV GB/s (decode) & TFLOP/s (multi-token) vs MI355X peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+ELT = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def work_model(w):
+    """Algorithmic bytes and flops of one step, per part of the path."""
+    elt = ELT[w.dtype]
+    kvb = w.kv_bytes_per_token()
+    n = w.n_new
+    L = w.context_lens.astype(np.int64)
+    dec = n == 1
+    mt = n > 1
+    row_q = int(n[dec].sum()) * w.num_q_heads * w.head_dim * elt
+    m = {}
+    m["rows_bytes"] = int((L[dec] * kvb).sum()) + 2 * row_q       # KV once per KV head + q + out
+    m["tile_bytes"] = int((L[mt] * kvb).sum()) + 2 * int(n[mt].sum()) * w.num_q_heads * w.head_dim * elt
+    m["tile_flops"] = int(4 * w.head_dim * w.num_q_heads *
+                          (n[mt] * (L[mt] - n[mt]) + n[mt] * (n[mt] + 1) // 2).sum())
+    m["write_bytes"] = 2 * int(w.k_new.shape[0]) * kvb
+    blk_bytes = w.num_kv_heads * w.block_size * w.head_dim * elt * 2
+    m["copy_bytes"] = 2 * int(w.cow_pairs.shape[0]) * blk_bytes
+    m["table_bytes"] = int(((L + w.block_size - 1) // w.block_size).sum()) * 4
+    m["step_bytes"] = (m["rows_bytes"] + m["tile_bytes"] + m["write_bytes"] + m["copy_bytes"]
+                       + m["table_bytes"])
+    return m
+
+
+def cpu_baseline(w, target_s: float):
+    """The oracle, as it stands, on a bounded sample of sequences."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    k, v = w.empty_pools()
+    oracle.write_kv(k, v, w.hist_k, w.hist_v, w.hist_slots)
+    oracle.copy_blocks(k, v, w.cow_pairs)
+    oracle.write_kv(k, v, w.k_new, w.v_new, w.slot_mapping)
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    kvb = w.kv_bytes_per_token()
+    elt = ELT[w.dtype]
+    done, nbytes, nflops, t_used = [], 0, 0, 0.0
+    for s in order:
+        n = int(w.n_new[s])
+        if n == 0:
+            continue
+        t0 = time.perf_counter()
+        oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                         w.num_kv_heads, w.dtype, w.scale, seqs=[int(s)])
+        t_used += time.perf_counter() - t0
+        L = int(w.context_lens[s])
+        done.append(int(s))
+        nbytes += L * kvb + 2 * n * w.num_q_heads * w.head_dim * elt
+        nflops += 4 * w.head_dim * w.num_q_heads * (n * (L - n) + n * (n + 1) // 2)
+        if t_used >= target_s:
+            break
+    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle attention over {len(done)} of {w.num_seqs} sequences "
+                      f"({nbytes / 1e6:.1f} MB KV+q+out, {nflops / 1e9:.2f} GFLOP) in {t_used:.1f} s",
+            "gflops": nflops / t_used / 1e9}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards by KV head or by sequence with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.step import DeviceBatch
+    from workloads import config_workload
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 3
+    t0 = time.time()
+    w = config_workload(args.config, args.seed)
+    print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    db = DeviceBatch(w, opt=binding.options(args.split))
+    db.write_history()
+    torch.cuda.synchronize()
+    model = work_model(w)
+    has_tiles = bool((w.n_new > 1).any()) and w.dtype != "f32" and w.block_size in (16, 32)
+    has_rows = bool((w.n_new == 1).any()) or (bool((w.n_new > 1).any()) and not has_tiles)
+    kernels = []
+    if has_tiles:
+        kernels.append(("tile", binding.PA_TIME_TILE))
+    if has_rows:
+        kernels.append(("rows", binding.PA_TIME_ROWS))
+    if has_tiles and w.dtype != "f32":
+        dominant = "tile" if model["tile_flops"] / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12) > \
+            model["rows_bytes"] / (HBM_PEAK_GBS * 1e9) else ("rows" if has_rows else "tile")
+    else:
+        dominant = "rows"
+
+    def run_step(opt):
+        db.copy_blocks()
+        db.write_new()
+        db.attention(opt=opt)
+
+    base_opt = binding.options(args.split)
+    for _ in range(args.warmup):
+        run_step(base_opt)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    K = args.steps
+    dom_id = dict(kernels)[dominant]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    opts = [binding.options(args.split, 0, 0, dom_id, a, b) for a, b in evs]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        run_step(opts[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    print(f"[bench] timed {K} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # The other kernels, timed the same way in a second pass (reported only).
+    per_kernel = {dominant: dom_ms}
+    for name, kid in kernels:
+        if name == dominant:
+            continue
+        evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(K)]
+        opts2 = [binding.options(args.split, 0, 0, kid, a, b) for a, b in evs2]
+        for i in range(K):
+            run_step(opts2[i])
+        torch.cuda.synchronize()
+        per_kernel[name] = float(np.mean([a.elapsed_time(b) for a, b in evs2]))
+
+    value = model["step_bytes"] / (ms_step * 1e-3) / 1e9
+    if dominant == "rows":
+        achieved = model["rows_bytes"] / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "row_attn_kernel", "algorithmic_bytes": model["rows_bytes"],
+                "avg_ms": round(dom_ms, 5)}
+    else:
+        achieved = model["tile_flops"] / (dom_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": "tile_attn_kernel",
+                "algorithmic_flops": model["tile_flops"], "avg_ms": round(dom_ms, 5)}
+    extra = {}
+    if "tile" in per_kernel:
+        extra["multi_token_tflops"] = round(model["tile_flops"] / (per_kernel["tile"] * 1e-3) / 1e12, 1)
+    if "rows" in per_kernel:
+        extra["decode_kv_gbs"] = round(model["rows_bytes"] / (per_kernel["rows"] * 1e-3) / 1e9, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        print(f"[bench] cpu baseline in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+        cpu = {k2: (round(v, 3) if isinstance(v, float) else v) for k2, v in cpu.items()}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "config": args.config, "seqs": w.num_seqs,
+                   "query_rows": int(w.q.shape[0]), "new_tokens": int(w.k_new.shape[0]),
+                   "cow_pairs": int(w.cow_pairs.shape[0]),
+                   "step_bytes": model["step_bytes"], "multi_token_flops": model["tile_flops"]},
+        "roofline": roof,
+        "kernels_ms": {k2: round(v, 5) for k2, v in per_kernel.items()},
+        "derived": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

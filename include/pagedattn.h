@@ -1,0 +1,213 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: exact causal attention over a
+ * KV cache split into fixed-size blocks, reached through per-sequence block
+ * tables, on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *  - "Stateful Large Language Model Serving with Pensieve" (papercache.org
+ *    summary), sections on attention (LLM与注意力机制), the multi-token
+ *    kernel over non-contiguous KV (多Token注意力内核运算原理, 融合因果掩码与
+ *    内核实现) and unified prefill/decode batches (统一Prefill和Generation
+ *    阶段的执行过程).
+ *  - "vLLM-SOSP23" (papers.lqhl.me), sections 核心方法 (block tables,
+ *    copy-on-write) and Kernel 层实现 (block write, paged attention, block
+ *    copy).
+ *  - the devpress.csdn.net article on vLLM, sections 1 (block table worked
+ *    example) and 2.1 (copy-on-write under parallel sampling).
+ *  - "PagedAttention" (lib.yinfer.top), section 数学表述.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Memory.  Every pointer argument marked "device" is device memory on the
+ *  current HIP device; "host" pointers are host memory.  The caller allocates
+ *  and owns all buffers.  The library keeps no state between calls and never
+ *  allocates device memory.
+ *  Streams.  All GPU work is enqueued on `stream` (0 = the null stream) and
+ *  every call returns without waiting for it; buffers must stay alive until
+ *  that work completes.  Host pointers are read during the call only.
+ *  Errors.  Every call returns a pa_status.  Argument errors are found on the
+ *  host before anything is enqueued; then nothing is enqueued.
+ *  pa_last_error() gives a thread-local message for the last non-OK status.
+ *  Launch failures give PA_ERR_HIP.
+ *
+ *  Element types: PA_F32 (binary32), PA_F16 (binary16), PA_BF16 (bfloat16).
+ *  Attention accumulates in fp32 and rounds its output once, to nearest even.
+ *
+ *  KV pools (one per layer, K and V separate; num_blocks physical blocks):
+ *    k_cache[num_blocks][num_kv_heads][block_size][head_dim]
+ *    v_cache[num_blocks][num_kv_heads][head_dim][block_size]
+ *  i.e. inside a block and head, K is token-major and V is head-dim-major.
+ *  A slot is block * block_size + offset.
+ *
+ *  Supported shapes: head_dim 64 or 128; block_size 4, 8, 16 or 32 for every
+ *  dtype (the MFMA multi-token path needs block_size 16 or 32 and a 16-bit
+ *  dtype; other cases take a vector-ALU path with the same results within
+ *  tolerance); num_q_heads a multiple of num_kv_heads with a group of 1, 2,
+ *  4, 8 or 16 query heads per KV head.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, bad count, n > context, ... */
+  PA_ERR_UNSUPPORTED = -2, /* dtype / head_dim / block_size / group not built */
+  PA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
+  PA_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+  PA_ERR_BOUNDS = -5       /* PA_VALIDATE=1 found an id or slot out of range */
+} pa_status;
+
+/* Shape and element type of a KV pool pair. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_cache_desc;
+
+/* Optional tuning knobs; pass NULL for the defaults.  Results do not depend
+ * on them beyond floating-point rounding order. */
+typedef struct {
+  /* Tokens per split of a single-token (decode) row's context; 0 = auto.
+   * Rounded up to a multiple of 64.  Each split yields a partial softmax
+   * state that a combine kernel merges. */
+  int32_t decode_split_tokens;
+  /* Tokens per split of a multi-token request's context; 0 = no split. */
+  int32_t prefill_split_tokens;
+  /* Bit 0: route every row through the vector-ALU row kernel (the MFMA
+   * multi-token kernel is skipped).  Other bits must be 0. */
+  int32_t flags;
+  /* Profiling hook: when timed_kernel is one of PA_TIME_* and that kernel is
+   * launched, timing_start / timing_end (caller-created hipEvent_t, may be
+   * NULL) are recorded on `stream` immediately before and after it. */
+  int32_t timed_kernel;
+  hipEvent_t timing_start;
+  hipEvent_t timing_end;
+} pa_options;
+
+enum { PA_TIME_NONE = 0, PA_TIME_TILE = 1, PA_TIME_ROWS = 2, PA_TIME_COMBINE = 3 };
+
+/*
+ * pa_write_kv -- slot-mapping scatter of new K/V into the pools.
+ *
+ * Pensieve page (统一Prefill和Generation阶段的执行过程): newly computed K and
+ * V of every batched token are stored into the cache slots allocated for them
+ * before attention runs.  vLLM-SOSP23 page (Kernel 层实现): the reshape and
+ * the block write are one fused kernel.
+ *
+ *  k_new, v_new   device, [num_tokens][num_kv_heads][head_dim], c->dtype.
+ *  slot_mapping   device int64 [num_tokens]; token t goes to block
+ *                 slot / block_size, offset slot % block_size.  A negative
+ *                 slot skips the token.  Slots >= num_blocks * block_size are
+ *                 skipped too (PA_VALIDATE=1 reports them as PA_ERR_BOUNDS).
+ *  k_cache, v_cache  device pools (layout above), written in place.
+ *  Precondition: slots within one call are distinct.  The copy is bit-exact.
+ *  num_tokens == 0 is valid and enqueues nothing.
+ */
+pa_status pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache,
+                      const pa_cache_desc* c, hipStream_t stream);
+
+/*
+ * pa_copy_blocks -- batched whole-block copy for copy-on-write.
+ *
+ * devpress.csdn.net vLLM article, section 2.1: a writer that finds its block
+ * shared (reference count > 1) gets a new physical block into which the old
+ * block is copied; vLLM-SOSP23 page (Kernel 层实现) names the batched block
+ * copy kernel.
+ *
+ *  block_pairs  device int32 [num_pairs][2] = (src, dst); for every pair both
+ *               K and V of all heads of block src are copied to block dst.
+ *               Pairs with an id outside [0, num_blocks) are skipped
+ *               (PA_VALIDATE=1 reports PA_ERR_BOUNDS).
+ *  Precondition: destinations are distinct and no destination is a source in
+ *  the same call, so pairs may run in any order.  Bit-exact.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* c,
+                         const int32_t* block_pairs, int32_t num_pairs, hipStream_t stream);
+
+/*
+ * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
+ * for a batch of num_seqs sequences, total_q query rows, and no context longer
+ * than max_context_len, with the given options (NULL = defaults).
+ */
+size_t pa_attention_workspace_size(const pa_cache_desc* c, int32_t num_q_heads,
+                                   int32_t num_seqs, int32_t total_q,
+                                   int32_t max_context_len, const pa_options* opt);
+
+/*
+ * pa_attention -- causal attention of a ragged batch over the paged cache.
+ *
+ * Pensieve page (LLM与注意力机制): A = Q K^T * scale, O = softmax(A) V per
+ * head.  "PagedAttention" page (数学表述): query i attends to keys up to its
+ * own position.  vLLM-SOSP23 page (核心方法): K/V are read by indirection
+ * through the block table, exactly, with no approximation.  Pensieve page
+ * (多Token注意力内核运算原理, 统一Prefill和Generation阶段的执行过程): a batch
+ * concatenates each request's new tokens -- one for a decode, many for a
+ * prefill -- and per-request auxiliary data delimits them; the causal mask is
+ * fused into the kernel.
+ *
+ *  out             device [total_q][num_q_heads][head_dim], c->dtype.
+ *  q               device [total_q][num_q_heads][head_dim], c->dtype.
+ *  k_cache,v_cache device pools (layout above); not modified.
+ *  num_q_heads     query heads; query head h reads KV head h / (num_q_heads /
+ *                  num_kv_heads).
+ *  block_tables    device int32 [num_seqs][max_blocks_per_seq]; entry j of
+ *                  row s is the physical block of tokens [j*bs, (j+1)*bs) of
+ *                  sequence s.  Entries at or beyond ceil(L_s / bs) are never
+ *                  read.  Ids must lie in [0, num_blocks).
+ *  context_lens    device int32 [num_seqs]: L_s, the context length including
+ *                  the sequence's new tokens (which pa_write_kv must already
+ *                  have stored).
+ *  query_start_loc device int32 [num_seqs + 1]: rows of sequence s are
+ *                  [qsl[s], qsl[s+1]); n_s = qsl[s+1] - qsl[s] new tokens,
+ *                  which are the last n_s context positions: row i of s
+ *                  attends to positions 0 .. L_s - n_s + i.  n_s = 0 is
+ *                  allowed.  qsl[0] must be 0 and qsl[num_seqs] = total_q.
+ *  context_lens_host, query_start_loc_host
+ *                  host mirrors of the two arrays above, with identical
+ *                  contents; used on the host for validation and launch
+ *                  sizing.
+ *  scale           multiplies q.k (usually 1/sqrt(head_dim)).
+ *  workspace       device, at least pa_attention_workspace_size(...) bytes,
+ *                  256-byte aligned; contents on entry are ignored.
+ *  opt             NULL or tuning options (same as given to the size query).
+ *  Errors: PA_ERR_INVALID_ARG if num_q_heads % num_kv_heads != 0, n_s > L_s,
+ *  qsl is not non-decreasing from 0 to total_q, or L_s > max_blocks_per_seq*bs;
+ *  PA_ERR_WORKSPACE if the workspace is too small.
+ *  Sub-requests (two query ranges over one context) are expressed by giving
+ *  two sequences the same block-table row with different context_lens and
+ *  query ranges.
+ */
+pa_status pa_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const pa_cache_desc* c, int32_t num_q_heads,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, const int32_t* query_start_loc,
+                       int32_t num_seqs, int32_t total_q,
+                       const int32_t* context_lens_host, const int32_t* query_start_loc_host,
+                       float scale, void* workspace, size_t workspace_bytes,
+                       const pa_options* opt, hipStream_t stream);
+
+/* Thread-local text of the last non-OK status returned on this thread. */
+const char* pa_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,178 @@
+"""ctypes binding of libpagedattn.so: argument marshalling only.
+
+Every function here takes torch tensors (for device memory and the current
+HIP stream), checks shapes and dtypes, and calls the C entry point of the
+same name.  No part of the computation happens in Python.  If the library
+has not been built the import raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
+          -4: "PA_ERR_HIP", -5: "PA_ERR_BOUNDS"}
+TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+SYMBOLS = ("pa_write_kv", "pa_copy_blocks", "pa_attention_workspace_size", "pa_attention",
+           "pa_last_error", "pa_version")
+
+
+class PaCacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class PaOptions(ctypes.Structure):
+    _fields_ = [("decode_split_tokens", ctypes.c_int32), ("prefill_split_tokens", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("timed_kernel", ctypes.c_int32),
+                ("timing_start", ctypes.c_void_p), ("timing_end", ctypes.c_void_p)]
+
+
+PA_TIME_NONE, PA_TIME_TILE, PA_TIME_ROWS, PA_TIME_COMBINE = 0, 1, 2, 3
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m paged_kv_cache_block_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+    desc_p = ctypes.POINTER(PaCacheDesc)
+    opt_p = ctypes.POINTER(PaOptions)
+    lib.pa_write_kv.argtypes = [vp, vp, i64p, i32, vp, vp, desc_p, vp]
+    lib.pa_write_kv.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [vp, vp, desc_p, i32p, i32, vp]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_attention_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, opt_p]
+    lib.pa_attention_workspace_size.restype = ctypes.c_size_t
+    lib.pa_attention.argtypes = [vp, vp, vp, vp, desc_p, i32, i32p, i32, i32p, i32p, i32, i32,
+                                 i32p, i32p, ctypes.c_float, vp, ctypes.c_size_t, opt_p, vp]
+    lib.pa_attention.restype = ctypes.c_int
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_int32
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PagedAttnError(status, LIB.pa_last_error().decode(errors="replace"))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> PaCacheDesc:
+    """Descriptor of a pool pair: K [NB][H][bs][D], V [NB][H][D][bs]."""
+    if k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("pools must be 4-D")
+    nb, h, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != (nb, h, d, bs):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} != {(nb, h, d, bs)}")
+    if k_cache.dtype != v_cache.dtype or k_cache.dtype not in TORCH_TO_PA:
+        raise ValueError("pools must share a dtype among float32, float16, bfloat16")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("pools must be contiguous")
+    return PaCacheDesc(nb, bs, h, d, TORCH_TO_PA[k_cache.dtype])
+
+
+def options(decode_split_tokens: int = 0, prefill_split_tokens: int = 0, flags: int = 0,
+            timed_kernel: int = 0, timing_start=None, timing_end=None):
+    """``timing_start`` / ``timing_end`` are ``torch.cuda.Event(enable_timing=True)``
+    objects (or raw hipEvent_t handles) recorded around ``timed_kernel``."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not isinstance(ev, int):
+            ev.record()          # materialise the underlying hipEvent_t
+            ev = ev.cuda_event
+        return ev
+    return PaOptions(decode_split_tokens, prefill_split_tokens, flags, timed_kernel,
+                     handle(timing_start), handle(timing_end))
+
+
+def pa_write_kv(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    desc = cache_desc(k_cache, v_cache)
+    t = int(k_new.shape[0])
+    for x in (k_new, v_new):
+        if tuple(x.shape) != (t, desc.num_kv_heads, desc.head_dim) or x.dtype != k_cache.dtype \
+                or not x.is_contiguous():
+            raise ValueError("k_new/v_new must be contiguous [T][H_kv][D] in the pool dtype")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (t,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(LIB.pa_write_kv(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), t, _ptr(k_cache),
+                           _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
+    desc = cache_desc(k_cache, v_cache)
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [n][2]")
+    _check(LIB.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                              _ptr(block_pairs.contiguous()), int(block_pairs.shape[0]),
+                              _stream(stream)))
+
+
+def pa_attention_workspace_size(desc: PaCacheDesc, num_q_heads: int, num_seqs: int, total_q: int,
+                                max_context_len: int, opt: PaOptions | None = None) -> int:
+    return int(LIB.pa_attention_workspace_size(ctypes.byref(desc), num_q_heads, num_seqs,
+                                               total_q, max_context_len,
+                                               ctypes.byref(opt) if opt is not None else None))
+
+
+def pa_attention(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                 context_lens_host, query_start_loc_host, scale: float, workspace,
+                 opt: PaOptions | None = None, stream=None) -> None:
+    """Causal paged attention of a ragged batch; writes ``out`` in place.
+
+    ``context_lens_host`` / ``query_start_loc_host`` are contiguous int32 CPU
+    tensors with the same contents as their device counterparts.
+    """
+    desc = cache_desc(k_cache, v_cache)
+    tq, hq, d = q.shape
+    if tuple(out.shape) != (tq, hq, d) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q/out must be [T_q][H_q][D] in the pool dtype")
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q/out must be contiguous")
+    s = int(context_lens.shape[0])
+    for x in (block_tables, context_lens, query_start_loc):
+        if x.dtype != torch.int32 or not x.is_contiguous():
+            raise ValueError("block_tables, context_lens, query_start_loc must be contiguous int32")
+    for x in (context_lens_host, query_start_loc_host):
+        if x.dtype != torch.int32 or x.device.type != "cpu" or not x.is_contiguous():
+            raise ValueError("host mirrors must be contiguous int32 CPU tensors")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or query_start_loc.shape[0] != s + 1:
+        raise ValueError("block_tables [S][max_blocks] and query_start_loc [S+1] expected")
+    _check(LIB.pa_attention(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                            hq, _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+                            _ptr(query_start_loc), s, tq, _ptr(context_lens_host),
+                            _ptr(query_start_loc_host), float(scale), _ptr(workspace),
+                            0 if workspace is None else int(workspace.numel() * workspace.element_size()),
+                            ctypes.byref(opt) if opt is not None else None, _stream(stream)))
+
+
+def version() -> int:
+    return int(LIB.pa_version())

@@ -1,0 +1,307 @@
+// C ABI of libpagedattn: argument checks, workspace layout, launch sizing.
+// Declarations and contracts are in include/pagedattn.h.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+using namespace pa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool validate_mode() {
+  const char* v = getenv("PA_VALIDATE");
+  return v && v[0] == '1';
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+pa_status check_desc(const pa_cache_desc* c, PoolArgs* p) {
+  if (!c) return fail(PA_ERR_INVALID_ARG, "cache descriptor is null");
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", c->head_dim);
+  if (c->block_size != 4 && c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (4, 8, 16, 32)", c->block_size);
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks and num_kv_heads must be positive");
+  *p = PoolArgs{c->num_blocks, c->block_size, c->num_kv_heads, c->head_dim, c->dtype};
+  return PA_OK;
+}
+
+// Copy a small device array to the host (used only under PA_VALIDATE=1).
+template <typename T>
+pa_status fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
+  dst.resize(n);
+  if (n == 0) return PA_OK;
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "PA_VALIDATE copy");
+  return PA_OK;
+}
+
+int effective_split(const pa_options* opt, bool for_bound) {
+  if (opt && opt->decode_split_tokens > 0) return (opt->decode_split_tokens + 63) / 64 * 64;
+  return for_bound ? kMinAutoSplit : kDefaultDecodeSplit;
+}
+
+bool vector_all(const PoolArgs& p, const pa_options* opt) {
+  return (opt && (opt->flags & 1)) || !tile_path_supported(p);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q, int max_len,
+                            const pa_options* opt) {
+  WorkspaceLayout w{};
+  const int split = effective_split(opt, true);
+  const bool va = vector_all(p, opt);
+  const int64_t row_rows = va ? total_q : std::min(num_seqs, total_q);
+  const int64_t max_splits = row_splits(std::max(max_len, 1), split);
+  const int group = hq / p.num_kv_heads;
+  w.cap_rows = row_rows * max_splits;
+  w.cap_combs = row_rows;
+  w.cap_partials = max_splits > 1 ? w.cap_rows : 0;
+  w.cap_tiles = va ? 0 : ((int64_t)total_q * group + kTileRows - 1) / kTileRows + num_seqs;
+  size_t off = 0;
+  w.counts = off; off = align256(off + sizeof(PlanCounts));
+  w.rows = off;   off = align256(off + sizeof(RowItem) * (size_t)w.cap_rows);
+  w.tiles = off;  off = align256(off + sizeof(TileItem) * (size_t)w.cap_tiles);
+  w.combs = off;  off = align256(off + sizeof(CombItem) * (size_t)w.cap_combs);
+  w.part_ml = off; off = align256(off + 8ull * (size_t)w.cap_partials * hq);
+  w.part_o = off;  off = align256(off + 4ull * (size_t)w.cap_partials * hq * p.head_dim);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_version(void) { return 100; }
+
+pa_status pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache, const pa_cache_desc* c,
+                      hipStream_t stream) {
+  PoolArgs p;
+  pa_status st = check_desc(c, &p);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
+  if (validate_mode()) {
+    std::vector<int64_t> slots;
+    if ((st = fetch(slots, slot_mapping, (size_t)num_tokens, stream)) != PA_OK) return st;
+    const int64_t total = (int64_t)p.num_blocks * p.block_size;
+    std::vector<int64_t> seen;
+    for (int64_t sl : slots) {
+      if (sl >= total) return fail(PA_ERR_BOUNDS, "slot %lld out of range", (long long)sl);
+      if (sl >= 0) seen.push_back(sl);
+    }
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+      return fail(PA_ERR_BOUNDS, "duplicate slot in slot_mapping");
+  }
+  hipError_t e = launch_write_kv(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, p, stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* c,
+                         const int32_t* block_pairs, int32_t num_pairs, hipStream_t stream) {
+  PoolArgs p;
+  pa_status st = check_desc(c, &p);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs < 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "K/V pools must be 16-byte aligned");
+  if (validate_mode()) {
+    std::vector<int32_t> pr;
+    if ((st = fetch(pr, block_pairs, 2 * (size_t)num_pairs, stream)) != PA_OK) return st;
+    std::vector<int32_t> dsts, srcs;
+    for (int i = 0; i < num_pairs; ++i) {
+      const int32_t a = pr[2 * i], b = pr[2 * i + 1];
+      if (a < 0 || a >= p.num_blocks || b < 0 || b >= p.num_blocks)
+        return fail(PA_ERR_BOUNDS, "block pair (%d, %d) out of range", a, b);
+      srcs.push_back(a);
+      dsts.push_back(b);
+    }
+    std::sort(dsts.begin(), dsts.end());
+    std::sort(srcs.begin(), srcs.end());
+    if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end())
+      return fail(PA_ERR_BOUNDS, "duplicate destination block");
+    for (int32_t d : dsts)
+      if (std::binary_search(srcs.begin(), srcs.end(), d))
+        return fail(PA_ERR_BOUNDS, "block %d is both a source and a destination", d);
+  }
+  hipError_t e = launch_copy_blocks(k_cache, v_cache, p, block_pairs, num_pairs, stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "copy_blocks launch");
+}
+
+size_t pa_attention_workspace_size(const pa_cache_desc* c, int32_t num_q_heads, int32_t num_seqs,
+                                   int32_t total_q, int32_t max_context_len,
+                                   const pa_options* opt) {
+  PoolArgs p;
+  if (check_desc(c, &p) != PA_OK || num_q_heads <= 0 || num_seqs < 0 || total_q < 0 ||
+      num_q_heads % p.num_kv_heads != 0)
+    return 0;
+  return make_layout(p, num_q_heads, num_seqs, total_q, max_context_len, opt).total;
+}
+
+pa_status pa_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const pa_cache_desc* c, int32_t num_q_heads, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
+                       const int32_t* context_lens_host, const int32_t* query_start_loc_host,
+                       float scale, void* workspace, size_t workspace_bytes,
+                       const pa_options* opt, hipStream_t stream) {
+  PoolArgs p;
+  pa_status st = check_desc(c, &p);
+  if (st != PA_OK) return st;
+  if (num_q_heads <= 0 || num_q_heads % p.num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, p.num_kv_heads);
+  const int group = num_q_heads / p.num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not supported", group);
+  if (num_seqs < 0 || total_q < 0) return fail(PA_ERR_INVALID_ARG, "negative num_seqs or total_q");
+  if (opt && (opt->flags & ~1)) return fail(PA_ERR_INVALID_ARG, "unknown option flags");
+  if (opt && (opt->decode_split_tokens < 0 || opt->prefill_split_tokens < 0))
+    return fail(PA_ERR_INVALID_ARG, "negative split length");
+  if (opt && (opt->timed_kernel < 0 || opt->timed_kernel > PA_TIME_COMBINE))
+    return fail(PA_ERR_INVALID_ARG, "unknown timed_kernel %d", opt->timed_kernel);
+  if (num_seqs > 0 && (!context_lens_host || !query_start_loc_host))
+    return fail(PA_ERR_INVALID_ARG, "host mirrors are required");
+  if (num_seqs > 0 && max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+
+  // Host-side checks of the ragged batch.
+  int max_len = 0;
+  if (num_seqs > 0 && query_start_loc_host[0] != 0)
+    return fail(PA_ERR_INVALID_ARG, "query_start_loc[0] must be 0");
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
+    const int L = context_lens_host[s];
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, "query_start_loc decreases at sequence %d", s);
+    if (L < 0) return fail(PA_ERR_INVALID_ARG, "negative context length at sequence %d", s);
+    if (n > L) return fail(PA_ERR_INVALID_ARG, "sequence %d has %d new tokens but context %d", s, n, L);
+    if ((int64_t)L > (int64_t)max_blocks_per_seq * p.block_size)
+      return fail(PA_ERR_INVALID_ARG, "sequence %d context %d exceeds its block table", s, L);
+    max_len = std::max(max_len, L);
+  }
+  if ((num_seqs > 0 && query_start_loc_host[num_seqs] != total_q) || (num_seqs == 0 && total_q != 0))
+    return fail(PA_ERR_INVALID_ARG, "query_start_loc[num_seqs] != total_q");
+  if (total_q == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "q, out and the pools must be 16-byte aligned");
+
+  const WorkspaceLayout lay = make_layout(p, num_q_heads, num_seqs, total_q, max_len, opt);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, lay.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  if (validate_mode()) {
+    std::vector<int32_t> bt, lens, qsl;
+    if ((st = fetch(bt, block_tables, (size_t)num_seqs * max_blocks_per_seq, stream)) != PA_OK) return st;
+    if ((st = fetch(lens, context_lens, (size_t)num_seqs, stream)) != PA_OK) return st;
+    if ((st = fetch(qsl, query_start_loc, (size_t)num_seqs + 1, stream)) != PA_OK) return st;
+    for (int s = 0; s < num_seqs; ++s) {
+      if (lens[s] != context_lens_host[s] || qsl[s + 1] != query_start_loc_host[s + 1])
+        return fail(PA_ERR_BOUNDS, "device and host batch descriptions differ at sequence %d", s);
+      const int nb = (lens[s] + p.block_size - 1) / p.block_size;
+      for (int j = 0; j < nb; ++j) {
+        const int32_t b = bt[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= p.num_blocks)
+          return fail(PA_ERR_BOUNDS, "block_tables[%d][%d] = %d out of range", s, j, b);
+      }
+    }
+  }
+
+  // Launch sizes: the same counts the plan kernel derives on the device.
+  const bool va = vector_all(p, opt);
+  const int split = effective_split(opt, false);
+  int64_t n_rows = 0, n_tiles = 0, n_combs = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
+    const int L = context_lens_host[s];
+    const SeqWork w = seq_work(n, va ? 1 : 0, group, kTileRows);
+    for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
+      const int ns = row_splits(L - n + i + 1, split);
+      n_rows += ns;
+      if (ns > 1) n_combs += 1;
+    }
+    n_tiles += w.tiles;
+  }
+  if (n_rows > lay.cap_rows || n_tiles > lay.cap_tiles || n_combs > lay.cap_combs)
+    return fail(PA_ERR_WORKSPACE, "plan exceeds workspace capacity");
+  if (n_rows > 0x7fffffff || n_tiles > 0x7fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
+
+  PlanParams pp{num_seqs, split, group, va ? 1 : 0,
+                lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials};
+  hipError_t e = launch_plan(context_lens, query_start_loc, pp, workspace, lay, stream);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+
+  AttnArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+             max_blocks_per_seq, num_q_heads, total_q, scale * kLog2e, workspace};
+  // Optional events around one kernel, recorded on `stream` (profiling hook).
+  const int timed = opt ? opt->timed_kernel : 0;
+  auto mark = [&](int which, hipEvent_t ev) {
+    if (timed == which && ev) (void)hipEventRecord(ev, stream);
+  };
+  if (n_tiles > 0) {
+    mark(PA_TIME_TILE, opt ? opt->timing_start : nullptr);
+    if ((e = launch_tile_attention(a, p, lay, (int)n_tiles, stream)) != hipSuccess)
+      return hip_fail(e, "multi-token attention launch");
+    mark(PA_TIME_TILE, opt ? opt->timing_end : nullptr);
+  }
+  if (n_rows > 0) {
+    mark(PA_TIME_ROWS, opt ? opt->timing_start : nullptr);
+    if ((e = launch_row_attention(a, p, lay, (int)n_rows, split, stream)) != hipSuccess)
+      return hip_fail(e, "row attention launch");
+    mark(PA_TIME_ROWS, opt ? opt->timing_end : nullptr);
+  }
+  if (n_combs > 0) {
+    mark(PA_TIME_COMBINE, opt ? opt->timing_start : nullptr);
+    if ((e = launch_combine(a, p, lay, (int)n_combs, stream)) != hipSuccess)
+      return hip_fail(e, "split combine launch");
+    mark(PA_TIME_COMBINE, opt ? opt->timing_end : nullptr);
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// Device helpers shared by the gfx950 kernels of libpagedattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+template <int DT> struct Elt;
+template <> struct Elt<DT_F32> { static constexpr int bytes = 4; using store_t = uint32_t; };
+template <> struct Elt<DT_F16> { static constexpr int bytes = 2; using store_t = uint16_t; };
+template <> struct Elt<DT_BF16> { static constexpr int bytes = 2; using store_t = uint16_t; };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- element <-> float ----------------------------------------------------
+template <int DT> __device__ __forceinline__ float lo_to_float(uint32_t w);
+template <int DT> __device__ __forceinline__ float hi_to_float(uint32_t w);
+
+template <> __device__ __forceinline__ float lo_to_float<DT_F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <> __device__ __forceinline__ float hi_to_float<DT_F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+template <> __device__ __forceinline__ float lo_to_float<DT_BF16>(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+template <> __device__ __forceinline__ float hi_to_float<DT_BF16>(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// Unpack 4 bytes-per-word storage into floats: N words -> N (f32) or 2N values.
+template <int DT, int NW>
+__device__ __forceinline__ void unpack(const uint32_t (&w)[NW], float* out) {
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) out[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      out[2 * i] = lo_to_float<DT>(w[i]);
+      out[2 * i + 1] = hi_to_float<DT>(w[i]);
+    }
+  }
+}
+
+// float -> storage bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32: RNE
+}
+template <int DT> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == DT_F16)
+    return (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(b) << 16);
+  else
+    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// ---- wave reductions ------------------------------------------------------
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < WIDTH; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- workspace plan records ------------------------------------------------
+// One vector-ALU work item: a query row (seq, i) and one split of its keys.
+struct RowItem {
+  int32_t seq;
+  int32_t i;       // row index within the sequence's new tokens
+  int32_t split;   // split index
+  int32_t pslot;   // first partial slot of the row, or -1 if it has one split
+};
+// One MFMA work item: a tile of packed (token, head) rows of one sequence.
+struct TileItem {
+  int32_t seq;
+  int32_t tile;
+};
+// One combine item: a row whose splits must be merged.
+struct CombItem {
+  int32_t row;     // global query row
+  int32_t pslot;
+  int32_t nsplit;
+  int32_t seq;
+};
+struct PlanCounts {
+  int32_t rows, tiles, combs, partials;
+};
+
+}  // namespace pa
+
+namespace pa {
+
+// Work a sequence contributes to the plan.  The host (for launch sizes) and
+// the plan kernel (for the item lists) both call this, so they agree.
+struct SeqWork {
+  int32_t row_first;  // first row index that goes to the row kernel
+  int32_t rows;       // rows that go to the row kernel
+  int32_t tiles;      // MFMA tiles
+};
+
+__host__ __device__ inline SeqWork seq_work(int n, int vector_all, int group, int tile_rows) {
+  SeqWork w{0, 0, 0};
+  if (n <= 0) return w;
+  if (vector_all || n == 1) {
+    w.rows = n;
+  } else {
+    w.tiles = (n * group + tile_rows - 1) / tile_rows;
+  }
+  return w;
+}
+
+// Splits of a row whose causal limit admits `keys` keys.
+__host__ __device__ inline int row_splits(int keys, int split_tokens) {
+  if (keys <= split_tokens) return 1;
+  return (keys + split_tokens - 1) / split_tokens;
+}
+
+}  // namespace pa

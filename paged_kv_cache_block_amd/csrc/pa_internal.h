@@ -1,0 +1,70 @@
+// Host-side declarations shared by the C ABI (pa_api.cpp) and the kernel
+// launch wrappers of libpagedattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa_device.h"
+
+namespace pa {
+
+// Rows of packed (token, head) pairs per MFMA workgroup: 4 waves x 32 rows.
+constexpr int kTileRows = 128;
+// Keys per MFMA iteration.
+constexpr int kTileKeys = 32;
+// Minimum split length the auto policy may choose; sizes the workspace bound.
+constexpr int kMinAutoSplit = 256;
+constexpr int kDefaultDecodeSplit = 512;
+
+struct PoolArgs {
+  int num_blocks, block_size, num_kv_heads, head_dim, dtype;
+};
+
+// Byte offsets of the plan inside the workspace and the capacities behind them.
+struct WorkspaceLayout {
+  size_t counts, rows, tiles, combs, part_ml, part_o, total;
+  int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
+};
+
+struct PlanParams {
+  int num_seqs;
+  int split_tokens;   // keys per split of a row-kernel row
+  int group;          // query heads per KV head
+  int vector_all;     // 1: every row goes to the row kernel
+  int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
+};
+
+hipError_t launch_write_kv(const void* k_new, const void* v_new, const int64_t* slots,
+                           int num_tokens, void* k_cache, void* v_cache, const PoolArgs& p,
+                           hipStream_t s);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const PoolArgs& p,
+                              const int32_t* pairs, int num_pairs, hipStream_t s);
+hipError_t launch_plan(const int32_t* context_lens, const int32_t* qsl, const PlanParams& pp,
+                       void* ws, const WorkspaceLayout& lay, hipStream_t s);
+
+struct AttnArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* qsl;
+  int max_blocks;
+  int num_q_heads;
+  int total_q;
+  float scale_log2;   // scale * log2(e)
+  void* ws;
+};
+
+hipError_t launch_row_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
+                                int num_items, int split_tokens, hipStream_t s);
+hipError_t launch_combine(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
+                          int num_combs, hipStream_t s);
+hipError_t launch_tile_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
+                                 int num_tiles, hipStream_t s);
+bool tile_path_supported(const PoolArgs& p);
+
+}  // namespace pa

@@ -1,0 +1,113 @@
+// Bit-exact KV movers: the slot-mapping scatter and the batched block copy.
+//
+// vLLM-SOSP23 page (Kernel 层实现): the reshape and block write of new K/V is
+// one fused kernel, and block copies for copy-on-write are batched into one
+// launch.  Pensieve page (统一Prefill和Generation阶段的执行过程): new K/V
+// go into their allocated slots before attention runs.
+//
+// Both kernels move 16-byte chunks.  K keeps the token-major row of the input,
+// so a (token, head) row lands as D * elt contiguous bytes.  V is head-dim
+// major inside a block, so a (token, head) row becomes D elements spaced
+// block_size apart; those stores are narrow, but every new token of a block in
+// one call shares its lines in L2, which merges them before they reach HBM.
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+template <int EB>
+__global__ __launch_bounds__(256) void write_kv_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    const int64_t* __restrict__ slots, int64_t total_chunks, int chunks_per_row, int H, int D,
+    int bs, int64_t total_slots, uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache) {
+  using store_t = typename Elt<EB == 4 ? DT_F32 : DT_F16>::store_t;
+  constexpr int VEC = 16 / EB;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total_chunks) return;
+  const int chunk = (int)(gid % chunks_per_row);
+  const int64_t th = gid / chunks_per_row;
+  const int h = (int)(th % H);
+  const int64_t t = th / H;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= total_slots) return;
+  const int64_t blk = slot / bs;
+  const int off = (int)(slot - blk * bs);
+
+  const uint4 kv = k_new[gid];
+  uint8_t* kdst = k_cache + (((blk * H + h) * bs + off) * (int64_t)D) * EB + (int64_t)chunk * 16;
+  *reinterpret_cast<uint4*>(kdst) = kv;
+
+  const uint4 vv = v_new[gid];
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  store_t* vdst = reinterpret_cast<store_t*>(v_cache) +
+                  ((blk * H + h) * (int64_t)D + (int64_t)chunk * VEC) * bs + off;
+  if constexpr (EB == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vdst[(int64_t)e * bs] = w[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vdst[(int64_t)(2 * e) * bs] = (uint16_t)(w[e] & 0xffffu);
+      vdst[(int64_t)(2 * e + 1) * bs] = (uint16_t)(w[e] >> 16);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t chunks_per_block,
+                                                          int num_blocks) {
+  const int p = blockIdx.x;
+  const int src = pairs[2 * p];
+  const int dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t s0 = (int64_t)src * chunks_per_block;
+  const int64_t d0 = (int64_t)dst * chunks_per_block;
+  for (int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x; c < chunks_per_block;
+       c += (int64_t)gridDim.y * 256) {
+    const uint4 a = k_cache[s0 + c];
+    const uint4 b = v_cache[s0 + c];
+    k_cache[d0 + c] = a;
+    v_cache[d0 + c] = b;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_write_kv(const void* k_new, const void* v_new, const int64_t* slots,
+                           int num_tokens, void* k_cache, void* v_cache, const PoolArgs& p,
+                           hipStream_t s) {
+  const int eb = p.dtype == DT_F32 ? 4 : 2;
+  const int cpr = p.head_dim * eb / 16;
+  const int64_t total = (int64_t)num_tokens * p.num_kv_heads * cpr;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  const int64_t total_slots = (int64_t)p.num_blocks * p.block_size;
+  if (eb == 4)
+    hipLaunchKernelGGL(write_kv_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s,
+                       (const uint4*)k_new, (const uint4*)v_new, slots, total, cpr,
+                       p.num_kv_heads, p.head_dim, p.block_size, total_slots,
+                       (uint8_t*)k_cache, (uint8_t*)v_cache);
+  else
+    hipLaunchKernelGGL(write_kv_kernel<2>, dim3((unsigned)grid), dim3(256), 0, s,
+                       (const uint4*)k_new, (const uint4*)v_new, slots, total, cpr,
+                       p.num_kv_heads, p.head_dim, p.block_size, total_slots,
+                       (uint8_t*)k_cache, (uint8_t*)v_cache);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const PoolArgs& p,
+                              const int32_t* pairs, int num_pairs, hipStream_t s) {
+  if (num_pairs == 0) return hipSuccess;
+  const int eb = p.dtype == DT_F32 ? 4 : 2;
+  const int64_t cpb = (int64_t)p.num_kv_heads * p.block_size * p.head_dim * eb / 16;
+  int gy = (int)((cpb + 255) / 256);
+  if (gy > 64) gy = 64;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, gy), dim3(256), 0, s,
+                     (uint4*)k_cache, (uint4*)v_cache, pairs, cpb, p.num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

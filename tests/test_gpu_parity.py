@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: scatter, block copy and indexing bit-exact; attention within
+max |d| <= 1e-5 for fp32 inputs, and max |d| <= 1e-2 with mean |d| <= 1e-3
+for fp16 / bf16 inputs (fp32 accumulation on the GPU, float64 in the oracle).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import build_batch, config_workload, small_workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (1e-2, 1e-3), "bf16": (1e-2, 1e-3)}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+def _step_mod():
+    from paged_kv_cache_block_amd import step
+    return step
+
+
+def oracle_step(w):
+    k, v = w.empty_pools()
+    oracle.write_kv(k, v, w.hist_k, w.hist_v, w.hist_slots)
+    oracle.copy_blocks(k, v, w.cow_pairs)
+    oracle.write_kv(k, v, w.k_new, w.v_new, w.slot_mapping)
+    return k, v
+
+
+def compare(got_storage, want64, dtype, rows=None, what=""):
+    got = oracle.to_f64(got_storage, dtype)
+    if rows is not None:
+        got, want64 = got[rows], want64[rows]
+    assert np.isfinite(got).all(), f"{what}: non-finite GPU output"
+    diff = np.abs(got - want64)
+    mx, mean = float(diff.max()), float(diff.mean())
+    tmax, tmean = TOL[dtype]
+    say(f"{what}: max|d|={mx:.3e} mean|d|={mean:.3e}")
+    assert mx <= tmax, f"{what}: max |d| {mx} > {tmax}"
+    assert mean <= tmean, f"{what}: mean |d| {mean} > {tmean}"
+
+
+def run_gpu(w, opt=None, write_history=True):
+    torch = pytest.importorskip("torch")
+    db = _step_mod().DeviceBatch(w, opt=opt)
+    if write_history:
+        db.write_history()
+    db.step()
+    torch.cuda.synchronize()
+    return db
+
+
+def bits(a):
+    return a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+
+
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_write_and_copy_bit_exact(torch_cuda, cfg):
+    w = small_workload(cfg)
+    say("write/copy", w.name)
+    db = run_gpu(w)
+    gk, gv = db.pools_numpy()
+    k, v = oracle_step(w)
+    assert np.array_equal(bits(gk), bits(k)), "K pool differs"
+    assert np.array_equal(bits(gv), bits(v)), "V pool differs"
+
+
+@pytest.mark.parametrize("mode", ["default", "split64", "rows"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_attention_small(torch_cuda, cfg, mode):
+    step = _step_mod()
+    from paged_kv_cache_block_amd import binding
+    opt = {"default": None, "split64": binding.options(64), "rows": binding.options(0, 0, 1)}[mode]
+    w = small_workload(cfg)
+    say("attention", w.name, mode)
+    db = run_gpu(w, opt)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    compare(db.out_numpy(), want, w.dtype, what=f"{w.name} [{mode}]")
+
+
+@pytest.mark.parametrize("seed", [100, 200, 300])
+@pytest.mark.parametrize("cfg", [1, 3, 5])
+def test_attention_small_seeds(torch_cuda, cfg, seed):
+    w = small_workload(cfg, seed + cfg) if cfg != 1 else config_workload(1, seed + 1)
+    say("attention seed", seed, w.name)
+    db = run_gpu(w)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    compare(db.out_numpy(), want, w.dtype, what=f"{w.name} seed {seed}")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_relabelled_pool_is_bit_identical(torch_cuda, cfg):
+    """Physical block ids do not change the result, bit for bit."""
+    w = small_workload(cfg)
+    say("relabel", w.name)
+    a = run_gpu(w).out_numpy()
+    perm = np.random.default_rng(cfg + 7).permutation(w.num_blocks)
+    bs = w.block_size
+
+    def remap_slots(sl):
+        sl = np.asarray(sl, dtype=np.int64)
+        return np.where(sl >= 0, perm[sl // bs] * bs + sl % bs, sl)
+    import copy
+    w2 = copy.copy(w)
+    w2.hist_slots = remap_slots(w.hist_slots)
+    w2.slot_mapping = remap_slots(w.slot_mapping)
+    w2.block_tables = perm[w.block_tables].astype(np.int32)
+    w2.cow_pairs = perm[w.cow_pairs].astype(np.int32).reshape(-1, 2)
+    b = run_gpu(w2).out_numpy()
+    assert np.array_equal(bits(a), bits(b))
+
+
+SHAPES = [  # (dtype, H_q, H_kv, D, block_size)
+    ("f16", 8, 8, 64, 16), ("f16", 8, 4, 128, 32), ("f16", 16, 4, 64, 32), ("f16", 32, 2, 128, 16),
+    ("bf16", 8, 8, 128, 16), ("bf16", 16, 8, 64, 16), ("bf16", 32, 4, 128, 32),
+    ("f32", 4, 4, 128, 16), ("f32", 8, 2, 64, 32), ("f32", 16, 1, 64, 8),
+    ("f16", 4, 2, 128, 8), ("bf16", 8, 1, 64, 4),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_shape_sweep(torch_cuda, shape):
+    dtype, hq, hkv, d, bs = shape
+    seqs = [(0, 1, 1), (47, 1, 1), (130, 1, 1), (0, 19, 1), (70, 45, 1), (5, 2, 1), (200, 1, 1)]
+    w = build_batch(f"sweep {shape}", dtype, hq, hkv, d, bs, 512, seqs, 21)
+    say("shape", shape)
+    db = run_gpu(w)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    compare(db.out_numpy(), want, w.dtype, what=f"shape {shape}")
+
+
+def test_split_lengths_agree(torch_cuda):
+    from paged_kv_cache_block_amd import binding
+    w = small_workload(5)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    for split in (64, 128, 192, 512, 4096):
+        say("split", split)
+        db = run_gpu(w, binding.options(split))
+        compare(db.out_numpy(), want, w.dtype, what=f"split {split}")
+
+
+def test_edge_cases(torch_cuda):
+    """Sequences with no new tokens, one-token contexts, prefills without
+    history, sub-requests sharing one block-table row, and a ragged tail."""
+    seqs = [(5, 0, 1), (0, 1, 1), (0, 2, 1), (40, 0, 1), (31, 33, 1), (0, 0, 1), (63, 1, 1)]
+    w = build_batch("edges bf16", "bf16", 16, 2, 64, 16, 256, seqs, 11)
+    # Sequence 5 becomes a sub-request of sequence 4: its first 9 positions
+    # recomputed as queries over themselves.
+    w.block_tables[5] = w.block_tables[4]
+    w.context_lens[5] = 9
+    lens = w.context_lens
+    n = np.diff(w.query_start_loc)
+    n[5] = 9
+    qsl = np.zeros_like(w.query_start_loc)
+    qsl[1:] = np.cumsum(n)
+    rng = np.random.default_rng(3)
+    from workloads import round_to_dtype
+    q = round_to_dtype(rng.standard_normal((int(qsl[-1]), 16, 64), dtype=np.float32), "bf16")
+    w.q, w.query_start_loc, w.context_lens = q, qsl.astype(np.int32), lens
+    say("edge cases", w.name)
+    db = run_gpu(w)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    compare(db.out_numpy(), want, w.dtype, what="edge cases")
+
+
+def test_empty_and_error_paths(torch_cuda, monkeypatch):
+    torch = torch_cuda
+    from paged_kv_cache_block_amd import binding
+    w = small_workload(2)
+    db = _step_mod().DeviceBatch(w)
+    db.write_history()
+    say("validate: block id out of range")
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    bad = db.block_tables.clone()
+    bad[0, 0] = w.num_blocks + 5
+    with pytest.raises(binding.PagedAttnError) as ei:
+        binding.pa_attention(db.out, db.q, db.k_cache, db.v_cache, bad, db.context_lens,
+                             db.query_start_loc, db.context_lens_host, db.qsl_host, w.scale,
+                             db.workspace)
+    assert ei.value.status == -5
+    say("validate: duplicate slot")
+    dup = db.slot_mapping.clone()
+    dup[1] = dup[0]
+    with pytest.raises(binding.PagedAttnError) as ei:
+        binding.pa_write_kv(db.k_new, db.v_new, dup, db.k_cache, db.v_cache)
+    assert ei.value.status == -5
+    monkeypatch.delenv("PA_VALIDATE")
+    say("workspace too small")
+    with pytest.raises(binding.PagedAttnError) as ei:
+        binding.pa_attention(db.out, db.q, db.k_cache, db.v_cache, db.block_tables,
+                             db.context_lens, db.query_start_loc, db.context_lens_host,
+                             db.qsl_host, w.scale, db.workspace[:64])
+    assert ei.value.status == -3
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads: every output finite; sampled sequences vs the oracle
+# --------------------------------------------------------------------------
+def _sample(w, k):
+    rng = np.random.default_rng(12345)
+    n = w.n_new
+    mt = np.flatnonzero(n > 1)
+    dec = np.flatnonzero(n == 1)
+    pick = list(rng.choice(dec, size=min(k, dec.size), replace=False)) if dec.size else []
+    if mt.size:
+        pick += list(rng.choice(mt, size=min(2, mt.size), replace=False))
+    return sorted(int(s) for s in pick)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_config_sampled(torch_cuda, cfg):
+    w = config_workload(cfg)
+    say("full", w.name)
+    db = run_gpu(w)
+    got = db.out_numpy()
+    assert np.isfinite(oracle.to_f64(got, w.dtype)).all(), "non-finite output"
+    k, v = oracle_step(w)
+    seqs = _sample(w, 6)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale, seqs=seqs)
+    rows = np.concatenate([np.arange(w.query_start_loc[s], w.query_start_loc[s + 1]) for s in seqs])
+    compare(got, want, w.dtype, rows=rows, what=f"{w.name} sampled seqs {seqs}")
+    if cfg == 4:   # copy-on-write blocks bit-exact at full size
+        gk, gv = db.pools_numpy()
+        dst = w.cow_pairs[:, 1]
+        assert np.array_equal(bits(gk[dst]), bits(k[dst]))
+        assert np.array_equal(bits(gv[dst]), bits(v[dst]))
