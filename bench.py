@@ -177,11 +177,13 @@ def main(argv=None) -> int:
         per_kernel[name] = float(np.mean([a.elapsed_time(b) for a, b in evs2]))
 
     value = model["step_bytes"] / (ms_step * 1e-3) / 1e9
+    rows_kernel = ("decode_mfma_kernel" if w.dtype != "f32" and w.block_size in (16, 32)
+                   else "row_attn_kernel")
     if dominant == "rows":
         achieved = model["rows_bytes"] / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "row_attn_kernel", "algorithmic_bytes": model["rows_bytes"],
+                "kernel": rows_kernel, "algorithmic_bytes": model["rows_bytes"],
                 "avg_ms": round(dom_ms, 5)}
     else:
         achieved = model["tile_flops"] / (dom_ms * 1e-3) / 1e12

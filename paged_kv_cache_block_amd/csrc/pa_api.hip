@@ -65,9 +65,14 @@ pa_status fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
   return PA_OK;
 }
 
-int effective_split(const pa_options* opt, bool for_bound) {
+// Split length of row work.  `total_keys` is the sum over rows of the keys
+// each row attends to (only known at call time; -1 in size queries).
+int choose_split(const pa_options* opt, int64_t total_keys, int num_kv_heads) {
   if (opt && opt->decode_split_tokens > 0) return (opt->decode_split_tokens + 63) / 64 * 64;
-  return for_bound ? kMinAutoSplit : kDefaultDecodeSplit;
+  if (total_keys < 0) return kMinAutoSplit;
+  int64_t want = (total_keys * num_kv_heads + kAutoTargetWaves - 1) / kAutoTargetWaves;
+  want = (want + 63) / 64 * 64;
+  return (int)std::min<int64_t>(kMaxAutoSplit, std::max<int64_t>(kMinAutoSplit, want));
 }
 
 bool vector_all(const PoolArgs& p, const pa_options* opt) {
@@ -79,14 +84,21 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q, int max_len,
                             const pa_options* opt) {
   WorkspaceLayout w{};
-  const int split = effective_split(opt, true);
   const bool va = vector_all(p, opt);
   const int64_t row_rows = va ? total_q : std::min(num_seqs, total_q);
-  const int64_t max_splits = row_splits(std::max(max_len, 1), split);
   const int group = hq / p.num_kv_heads;
-  w.cap_rows = row_rows * max_splits;
+  if (opt && opt->decode_split_tokens > 0) {
+    const int split = choose_split(opt, -1, p.num_kv_heads);
+    w.cap_rows = row_rows * row_splits(std::max(max_len, 1), split);
+  } else {
+    // Every row has at most keys/split + 1 splits.  With the automatic split,
+    // sum(keys)/split <= kAutoTargetWaves / H_kv unless the split is clamped at
+    // kMaxAutoSplit, where sum(keys)/split <= rows * max_len / kMaxAutoSplit.
+    w.cap_rows = row_rows + (kAutoTargetWaves + p.num_kv_heads - 1) / p.num_kv_heads +
+                 row_rows * ((std::max(max_len, 1) + kMaxAutoSplit - 1) / kMaxAutoSplit);
+  }
   w.cap_combs = row_rows;
-  w.cap_partials = max_splits > 1 ? w.cap_rows : 0;
+  w.cap_partials = w.cap_rows;
   w.cap_tiles = va ? 0 : ((int64_t)total_q * group + kTileRows - 1) / kTileRows + num_seqs;
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(PlanCounts));
@@ -253,7 +265,14 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
 
   // Launch sizes: the same counts the plan kernel derives on the device.
   const bool va = vector_all(p, opt);
-  const int split = effective_split(opt, false);
+  int64_t total_keys = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
+    const int L = context_lens_host[s];
+    const SeqWork w = seq_work(n, va ? 1 : 0, group, kTileRows);
+    for (int i = w.row_first; i < w.row_first + w.rows; ++i) total_keys += L - n + i + 1;
+  }
+  const int split = choose_split(opt, total_keys, p.num_kv_heads);
   int64_t n_rows = 0, n_tiles = 0, n_combs = 0;
   for (int s = 0; s < num_seqs; ++s) {
     const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
@@ -291,8 +310,10 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   }
   if (n_rows > 0) {
     mark(PA_TIME_ROWS, opt ? opt->timing_start : nullptr);
-    if ((e = launch_row_attention(a, p, lay, (int)n_rows, split, stream)) != hipSuccess)
-      return hip_fail(e, "row attention launch");
+    e = (!va && decode_mfma_supported(p, group))
+            ? launch_decode_mfma(a, p, lay, (int)n_rows, split, stream)
+            : launch_row_attention(a, p, lay, (int)n_rows, split, stream);
+    if (e != hipSuccess) return hip_fail(e, "row attention launch");
     mark(PA_TIME_ROWS, opt ? opt->timing_end : nullptr);
   }
   if (n_combs > 0) {

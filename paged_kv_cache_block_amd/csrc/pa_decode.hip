@@ -1,0 +1,260 @@
+// MFMA decode attention (gfx950, fp16 / bf16): one query token per row.
+//
+// vLLM-SOSP23 page (核心方法, Kernel 层实现) and Pensieve page (多Token注意力
+// 内核运算原理): a decode token's attention is two matrix-vector products over
+// a paged context, read block by block through the block table.  Decode is
+// bound by HBM (vLLM blog page, 挑战), so the design goal is that every byte of
+// K and V is read once per KV head and that enough of them are in flight.
+//
+// One wavefront owns one (sequence, KV head, key split).  The up-to-16 query
+// heads of the KV head's group form the columns of 16x16 MFMA tiles, so a K/V
+// load serves all of them:
+//   S^T[key][head]  = K[key][:] . Q[head][:]      v_mfma_f32_16x16x32_{f16,bf16}
+//   online softmax per head (a head is one lane column of S^T)
+//   O^T[d][head]   += V^T[d][key] . P^T[key][head]
+// Both MFMA A operands are read straight from HBM into registers:
+//   K is token-major, so lane (row r, k-group c) loads 16 bytes of one key row;
+//   V is head-dim-major inside a block, so lane (row d, k-group c) loads the
+//   8 consecutive keys 8c..8c+7 of head-dim row d.
+// The K rows are permuted so the four S^T values a lane gets from each of the
+// two key tiles are exactly the 8 consecutive keys its P^T operand needs.
+// Keys go 32 per step, double-buffered: the next step's K and V loads are in
+// flight while the current step computes.  No LDS is used.
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int D>
+struct Stage {
+  u32x4 k[2][D / 32];   // two 16-key tiles x (D/32) k-steps
+  u32x4 v[D / 16];      // D/16 head-dim tiles, 8 keys each
+};
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
+                                                         WorkspaceLayout lay, int split_tokens) {
+  constexpr int KS = D / 32;
+  constexpr int NDT = D / 16;
+  static_assert(BS == 16 || BS == 32, "block size");
+
+  const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
+  const PlanCounts* pc = reinterpret_cast<const PlanCounts*>(ws + lay.counts);
+  if ((int)blockIdx.x >= pc->rows) return;
+  const RowItem it = reinterpret_cast<const RowItem*>(ws + lay.rows)[blockIdx.x];
+
+  const int lane = threadIdx.x;
+  const int c16 = lane & 15;       // MFMA row of A / column of B and C
+  const int grp = lane >> 4;       // k-group of A and B; row group of C
+  const int g = blockIdx.y;
+  const int Hq = a.num_q_heads;
+  const int Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int s = it.seq;
+  const int q0 = a.qsl[s];
+  const int n = a.qsl[s + 1] - q0;
+  const int L = a.context_lens[s];
+  const int row = q0 + it.i;
+  if (row >= a.total_q) return;
+  const int t0 = it.split * split_tokens;
+  const int t1 = min(L - n + it.i + 1, t0 + split_tokens);
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+  const unsigned nb_max = p.num_blocks - 1;
+  const int tb_max = a.max_blocks - 1;
+  const bool head_ok = c16 < G;
+  const int head = g * G + (head_ok ? c16 : 0);
+
+  // Q^T operand: column c16 is query head g*G + c16; k-group grp covers
+  // head-dim elements 32ks + 8grp .. +8.
+  u32x4 qreg[KS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * Hq + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = head_ok ? *reinterpret_cast<const u32x4*>(qp + 32 * ks + 8 * grp)
+                         : u32x4{0, 0, 0, 0};
+  }
+
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
+  // Key offsets within a 32-key step: A row c16 of key tile u holds key
+  // 8*(c16>>2) + 4u + (c16&3); lane group grp's V operand holds keys 8grp..8grp+7.
+  const int krow0 = 8 * (c16 >> 2) + (c16 & 3);
+  const int vkey = 8 * grp;
+
+  auto load = [&](int c0, Stage<D>& st) {
+    const unsigned b0 = min((unsigned)bt[min(c0 / BS, tb_max)], nb_max);
+    unsigned b1 = b0;
+    if constexpr (BS == 16) b1 = min((unsigned)bt[min(c0 / BS + 1, tb_max)], nb_max);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kk = krow0 + 4 * u;                       // 0..31
+      const unsigned blk = (BS == 16 && kk >= 16) ? b1 : b0;
+      const int off = (c0 + kk) % BS;
+      const uint16_t* kp = kc + (((int64_t)blk * Hkv + g) * BS + off) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) st.k[u][ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
+    }
+    {
+      const unsigned blk = (BS == 16 && vkey >= 16) ? b1 : b0;
+      const int off = (c0 + vkey) % BS;
+      const uint16_t* vp = vc + (((int64_t)blk * Hkv + g) * D + c16) * BS + off;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        st.v[dt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)16 * dt * BS);
+    }
+  };
+
+  f32x4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute = [&](int c0, Stage<D>& st) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc[u] = mfma16<DT>(st.k[u][ks], qreg[ks], sacc[u]);
+    }
+    // This lane holds head c16's scores for keys c0 + 8grp + (4u + i).
+    const bool tail = c0 + 32 > t1;
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = sacc[u][i] * a.scale_log2;
+        if (tail && c0 + vkey + 4 * u + i >= t1) x = -INFINITY;
+        sv[4 * u + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);           // finite: key c0 < t1
+    const float alpha = fast_exp2(m_run - m_new);
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = fast_exp2(sv[e] - m_new);
+      rs += sv[e];
+    }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    u32x4 pb;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pb[w] = pack2<DT>(sv[2 * w], sv[2 * w + 1]);
+    if (tail) {
+      // Slots at or past t1 may be unwritten (NaN); zero them, never multiply.
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t x = st.v[dt][w];
+          if (c0 + vkey + 2 * w >= t1) x &= 0xffff0000u;
+          if (c0 + vkey + 2 * w + 1 >= t1) x &= 0x0000ffffu;
+          st.v[dt][w] = x;
+        }
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] *= alpha;
+      o[dt] = mfma16<DT>(st.v[dt], pb, o[dt]);
+    }
+  };
+
+  Stage<D> sa, sb;
+  int c0 = t0;
+  load(c0, sa);
+  while (true) {
+    if (c0 + 32 < t1) load(c0 + 32, sb);
+    compute(c0, sa);
+    c0 += 32;
+    if (c0 >= t1) break;
+    if (c0 + 32 < t1) load(c0 + 32, sa);
+    compute(c0, sb);
+    c0 += 32;
+    if (c0 >= t1) break;
+  }
+
+  if (!head_ok) return;
+  if (it.pslot < 0) {
+    const float inv = 1.f / l_run;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)row * Hq + head) * D + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 w;
+      w.x = pack2<DT>(o[dt][0] * inv, o[dt][1] * inv);
+      w.y = pack2<DT>(o[dt][2] * inv, o[dt][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+    }
+  } else {
+    const int64_t slot = it.pslot + it.split;
+    if (slot >= lay.cap_partials) return;
+    float* po = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + lay.part_o) +
+                (slot * Hq + head) * D + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (grp == 0) {
+      float2* pm = reinterpret_cast<float2*>(const_cast<uint8_t*>(ws) + lay.part_ml);
+      pm[slot * Hq + head] = make_float2(m_run, l_run);
+    }
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay, int items,
+                    int split, hipStream_t s) {
+  const dim3 grid(items, p.num_kv_heads);
+  if (p.block_size == 16)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 16>), grid, dim3(64), 0, s, a, p, lay, split);
+  else if (p.block_size == 32)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 32>), grid, dim3(64), 0, s, a, p, lay, split);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_mfma_supported(const PoolArgs& p, int group) {
+  return (p.dtype == DT_F16 || p.dtype == DT_BF16) && (p.block_size == 16 || p.block_size == 32) &&
+         (p.head_dim == 64 || p.head_dim == 128) && group <= 16;
+}
+
+hipError_t launch_decode_mfma(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
+                              int num_items, int split_tokens, hipStream_t s) {
+  if (num_items == 0) return hipSuccess;
+  if (p.dtype == DT_F16) {
+    if (p.head_dim == 64) return launch_d<DT_F16, 64>(a, p, lay, num_items, split_tokens, s);
+    if (p.head_dim == 128) return launch_d<DT_F16, 128>(a, p, lay, num_items, split_tokens, s);
+  } else if (p.dtype == DT_BF16) {
+    if (p.head_dim == 64) return launch_d<DT_BF16, 64>(a, p, lay, num_items, split_tokens, s);
+    if (p.head_dim == 128) return launch_d<DT_BF16, 128>(a, p, lay, num_items, split_tokens, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -14,9 +14,12 @@ namespace pa {
 constexpr int kTileRows = 128;
 // Keys per MFMA iteration.
 constexpr int kTileKeys = 32;
-// Minimum split length the auto policy may choose; sizes the workspace bound.
-constexpr int kMinAutoSplit = 256;
-constexpr int kDefaultDecodeSplit = 512;
+// Automatic split length of single-row work: about kAutoTargetWaves
+// wavefronts over the whole batch, clamped to [kMinAutoSplit, kMaxAutoSplit]
+// keys and rounded to a multiple of 64.
+constexpr int kAutoTargetWaves = 8192;
+constexpr int kMinAutoSplit = 64;
+constexpr int kMaxAutoSplit = 1024;
 
 struct PoolArgs {
   int num_blocks, block_size, num_kv_heads, head_dim, dtype;
@@ -61,6 +64,9 @@ struct AttnArgs {
 
 hipError_t launch_row_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                                 int num_items, int split_tokens, hipStream_t s);
+bool decode_mfma_supported(const PoolArgs& p, int group);
+hipError_t launch_decode_mfma(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
+                              int num_items, int split_tokens, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                           int num_combs, hipStream_t s);
 hipError_t launch_tile_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
