@@ -10,16 +10,22 @@
 // row r is (new token r / G, query head g*G + r % G); all G query heads of a
 // KV head share each K/V tile.  Four wavefronts take 32 rows each.
 //
-// Per 32-key tile the workgroup stages K (token-major) and V (head-dim-major)
-// in LDS, then every wavefront computes, with v_mfma_f32_32x32x16_{f16,bf16}:
-//   S^T[key][row] = K[key][:] . Q[row][:]           (D/16 MFMAs)
+// Keys go 64 per iteration through a two-stage LDS ring: while the waves
+// compute on one stage, every thread holds the next tile's K/V chunks in
+// registers and writes them to the other stage afterwards; one barrier per
+// iteration.  Each wave computes, with v_mfma_f32_32x32x16_{f16,bf16}:
+//   S^T[key][row] = K[key][:] . Q[row][:]           (2 x D/16 MFMAs)
 //   online softmax per row (a row is one lane column of S^T, split over the
 //   two lane halves), causal mask from absolute key positions
-//   O^T[d][row]  += V^T[d][key] . P^T[key][row]      (D/32 x 2 MFMAs)
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row]      (D/32 x 4 MFMAs)
 // Working on the transposes keeps each row's statistics inside a lane pair
 // and lets both operands of the second product be read as 16-byte runs.
 // The K rows feeding S^T are permuted so that the eight keys a lane holds for
 // each P^T operand are consecutive, which is what the V^T operand reads.
+// The running max is only raised (and O rescaled) when a row's max grows by
+// more than 2^8, so most iterations skip the rescale.
+// Workgroups are numbered so that the tiles sharing one (sequence, KV head)
+// run on one XCD and reuse its L2.
 
 #include "pa_internal.h"
 
@@ -28,8 +34,14 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKeys = 64;          // keys per iteration
+constexpr int kTabWin = 256;       // block-table entries staged in LDS at a time
+constexpr float kLazyRescale = 8.f;  // log2 headroom before the running max moves
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -41,7 +53,19 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Key (within a 32-key tile) held by accumulator element e of lane half hh.
+// Two floats to two packed 16-bit values, round to nearest even (hardware).
+template <int DT>
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  if constexpr (DT == DT_F16) {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Key (within a 32-key half tile) held by accumulator element e of lane half hh.
 __device__ __forceinline__ int acc_key(int e, int hh) { return 16 * (e >> 3) + 8 * hh + (e & 7); }
 
 // Key whose K row is loaded as row r of the S^T product.  Row r of a 32x32
@@ -51,31 +75,48 @@ __device__ __forceinline__ int row_key(int r) {
   return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
 }
 
+// The other lane half's copy of x (lanes l and l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Logical work index of this workgroup: consecutive logical indices share
+// K/V, and each XCD (workgroups dispatched round-robin over 8) gets one
+// contiguous range of them.
+__device__ __forceinline__ int xcd_order(int bid, int n) {
+  const int xcd = bid & 7, pos = bid >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return xcd * per + min(xcd, rem) + pos;
+}
+
 template <int DT, int D, int BS>
-__global__ __launch_bounds__(256) void tile_attn_kernel(AttnArgs a, PoolArgs p,
-                                                       WorkspaceLayout lay) {
+__global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs p,
+                                                          WorkspaceLayout lay, int num_tiles) {
   constexpr int KS = D / 16;        // k-steps of the QK product
   constexpr int NDT = D / 32;       // 32-row head-dim tiles of O^T
   constexpr int KROW = D + 8;       // LDS row stride of K (elements), padded
-  constexpr int VROW = 32 + 8;      // LDS row stride of V^T (elements), padded
-  constexpr int KCH = D / 64;       // 16-byte K chunks per thread per tile
-  constexpr int VCH = D / 64;       // 16-byte V chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[32 * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[D * VROW];
+  constexpr int VROW = kKeys + 8;   // LDS row stride of V^T (elements), padded
+  constexpr int KCH = kKeys * D / 8 / 256;   // 16-byte K chunks per thread per tile
+  constexpr int VCH = D * kKeys / 8 / 256;   // 16-byte V chunks per thread per tile
+  constexpr int KSTAGE = kKeys * KROW;
+  constexpr int VSTAGE = D * VROW;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VSTAGE];
+  __shared__ unsigned btab[kTabWin];
 
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
   const PlanCounts* pc = reinterpret_cast<const PlanCounts*>(ws + lay.counts);
-  if ((int)blockIdx.x >= pc->tiles) return;
-  const TileItem ti = reinterpret_cast<const TileItem*>(ws + lay.tiles)[blockIdx.x];
+  const int Hkv = p.num_kv_heads;
+  const int logical = xcd_order(blockIdx.x, gridDim.x);
+  const int g = logical / num_tiles;
+  const int item = logical - g * num_tiles;
+  if (item >= pc->tiles) return;
+  const TileItem ti = reinterpret_cast<const TileItem*>(ws + lay.tiles)[item];
 
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int lane = tid & 63;
   const int col = lane & 31;
   const int hh = lane >> 5;
-  const int g = blockIdx.y;
   const int Hq = a.num_q_heads;
-  const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int s = ti.seq;
   const int q0 = a.qsl[s];
@@ -84,8 +125,9 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(AttnArgs a, PoolArgs p,
   const int R = n * G;
   const int r0 = ti.tile * kTileRows;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
-  const int nb_max = p.num_blocks - 1;
+  const unsigned nb_max = p.num_blocks - 1;
   const int tb_max = a.max_blocks - 1;
+  const float c = a.scale_log2;
 
   // This lane's row.
   const int r = r0 + 32 * wv + col;
@@ -94,10 +136,12 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(AttnArgs a, PoolArgs p,
   const int hq = g * G + (row_ok ? r % G : 0);
   const int p_row = row_ok ? L - n + qi : -1;
   // Key ranges: the workgroup's and this wave's (rows ascend, so the last
-  // row of a range has the largest causal limit).
+  // row of a range has the largest causal limit, the first the smallest).
   const int kend = L - n + (min(R, r0 + kTileRows) - 1) / G + 1;
   const bool wave_on = r0 + 32 * wv < R;
+  const bool wave_full = r0 + 32 * wv + 32 <= R;
   const int wend = wave_on ? L - n + (min(R, r0 + 32 * wv + 32) - 1) / G + 1 : 0;
+  const int wfirst = wave_on ? L - n + (r0 + 32 * wv) / G : 0;
 
   // Q^T operand of the QK product: lane (col, hh) holds Q[row col][16ks+8hh .. +8].
   u32x4 qreg[KS];
@@ -120,29 +164,46 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(AttnArgs a, PoolArgs p,
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
   u32x4 kbuf[KCH], vbuf[VCH];
 
+  // The sequence's block ids, kTabWin at a time, clamped to the pool.  A
+  // 64-key tile never straddles two windows (kTabWin is a multiple of 64/BS).
+  int win = -1;
+  auto ensure_window = [&](int kt) {
+    const int w = (kt * kKeys / BS) / kTabWin;
+    if (w == win) return;
+    __syncthreads();
+    for (int i = tid; i < kTabWin; i += 256)
+      btab[i] = min((unsigned)bt[min(w * kTabWin + i, tb_max)], nb_max);
+    __syncthreads();
+    win = w;
+  };
+  auto block_of = [&](int kt0, int rel) -> unsigned {
+    return btab[(kt0 + rel) / BS - win * kTabWin];
+  };
   auto load_tile = [&](int kt) {
+    ensure_window(kt);
+    const int kt0 = kt * kKeys;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + 256 * c;
+    for (int j = 0; j < KCH; ++j) {
+      const int idx = tid + 256 * j;
       const int tok = idx / (D / 8);
       const int dc = idx % (D / 8);
-      const int key = kt * 32 + tok;
+      const int key = kt0 + tok;
       if (key < kend) {
-        const int blk = min((unsigned)bt[min(key / BS, tb_max)], (unsigned)nb_max);
-        kbuf[c] = *reinterpret_cast<const u32x4*>(
+        const unsigned blk = block_of(kt0, tok);
+        kbuf[j] = *reinterpret_cast<const u32x4*>(
             kc + (((int64_t)blk * Hkv + g) * BS + key % BS) * D + dc * 8);
       } else {
-        kbuf[c] = u32x4{0, 0, 0, 0};
+        kbuf[j] = u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + 256 * c;
-      const int d = idx >> 2;
-      const int tc = idx & 3;
-      const int key0 = kt * 32 + tc * 8;
+    for (int j = 0; j < VCH; ++j) {
+      const int idx = tid + 256 * j;
+      const int d = idx >> 3;
+      const int kc8 = idx & 7;
+      const int key0 = kt0 + kc8 * 8;
       if (key0 < kend) {
-        const int blk = min((unsigned)bt[min(key0 / BS, tb_max)], (unsigned)nb_max);
+        const unsigned blk = block_of(kt0, kc8 * 8);
         u32x4 v = *reinterpret_cast<const u32x4*>(
             vc + (((int64_t)blk * Hkv + g) * D + d) * BS + key0 % BS);
         if (key0 + 8 > kend) {       // unwritten slots may hold NaN
@@ -154,90 +215,109 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(AttnArgs a, PoolArgs p,
             v[w] = x;
           }
         }
-        vbuf[c] = v;
+        vbuf[j] = v;
       } else {
-        vbuf[c] = u32x4{0, 0, 0, 0};
+        vbuf[j] = u32x4{0, 0, 0, 0};
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int stage) {
+    uint16_t* kd = Ks + stage * KSTAGE;
+    uint16_t* vd = Vs + stage * VSTAGE;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + 256 * c;
-      *reinterpret_cast<u32x4*>(&Ks[(idx / (D / 8)) * KROW + (idx % (D / 8)) * 8]) = kbuf[c];
+    for (int j = 0; j < KCH; ++j) {
+      const int idx = tid + 256 * j;
+      *reinterpret_cast<u32x4*>(&kd[(idx / (D / 8)) * KROW + (idx % (D / 8)) * 8]) = kbuf[j];
     }
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + 256 * c;
-      *reinterpret_cast<u32x4*>(&Vs[(idx >> 2) * VROW + (idx & 3) * 8]) = vbuf[c];
+    for (int j = 0; j < VCH; ++j) {
+      const int idx = tid + 256 * j;
+      *reinterpret_cast<u32x4*>(&vd[(idx >> 3) * VROW + (idx & 7) * 8]) = vbuf[j];
     }
   };
 
-  const int ntiles = (kend + 31) / 32;
+  const int ntiles = (kend + kKeys - 1) / kKeys;
   const int krow = row_key(col);
   load_tile(0);
+  store_tile(0);
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
+    const int stage = kt & 1;
     if (kt + 1 < ntiles) load_tile(kt + 1);
-    const int kt0 = kt * 32;
-    if (!wave_on || kt0 >= wend) continue;
-
-    // S^T = K . Q^T
-    f32x16 sacc;
+    const int kt0 = kt * kKeys;
+    if (wave_on && kt0 < wend) {
+      const uint16_t* ks_ = Ks + stage * KSTAGE;
+      const uint16_t* vs_ = Vs + stage * VSTAGE;
+      // S^T = K . Q^T for keys kt0 + [0, 32) and kt0 + [32, 64).
+      f32x16 sacc[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(&Ks[krow * KROW + 16 * ks + 8 * hh]);
-      sacc = mfma32<DT>(ka, qreg[ks], sacc);
-    }
-
-    // Online softmax for row `col` (this lane holds 16 of its 32 keys).
-    float sv[16];
-    float mx = -INFINITY;
+        for (int e = 0; e < 16; ++e) sacc[u][e] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kt0 + acc_key(e, hh);
-      sv[e] = key <= p_row ? sacc[e] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[e]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float rs = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(
+              &ks_[(32 * u + krow) * KROW + 16 * ks + 8 * hh]);
+          sacc[u] = mfma32<DT>(ka, qreg[ks], sacc[u]);
+        }
+      }
+      // Causal mask (a select), only where some key passes some row's limit.
+      if (!wave_full || kt0 + kKeys - 1 > wfirst) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sv[e] = fast_exp2(sv[e] - m_use);
-      rs += sv[e];
-    }
-    rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
+          for (int e = 0; e < 16; ++e)
+            if (kt0 + 32 * u + acc_key(e, hh) > p_row) sacc[u][e] = -INFINITY;
+      }
+      // Row max of this tile (raw scores), both lane halves.
+      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
-
-    // P^T operands: keys 8hh..8hh+7 and 16+8hh..16+8hh+7 of the tile.
-    u32x4 pb[2];
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_cand = mx * c;
+      const bool raise = m_cand > m_run + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? m_cand : m_run;
+        const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 on the first raise
+        l_run *= alpha;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pb[st][w] = pack2<DT>(sv[8 * st + 2 * w], sv[8 * st + 2 * w + 1]);
-
-    // O^T += V^T . P^T
+        for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float rs = 0.f;
+      u32x4 pb[4];
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4*>(&Vs[(32 * t + col) * VROW + 16 * st + 8 * hh]);
-        o[t] = mfma32<DT>(va, pb[st], o[t]);
+        for (int e = 0; e < 16; ++e) {
+          const float pe = fast_exp2(fmaf(sacc[u][e], c, -m_use));
+          sacc[u][e] = pe;
+          rs += pe;
+        }
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            pb[2 * u + v2][w] = cvt2<DT>(sacc[u][8 * v2 + 2 * w], sacc[u][8 * v2 + 2 * w + 1]);
+      }
+      rs += swap_halves(rs);
+      l_run += rs;
+      // O^T += V^T . P^T over 4 k-steps of 16 keys.
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const u32x4 va = *reinterpret_cast<const u32x4*>(
+              &vs_[(32 * t + col) * VROW + 16 * st + 8 * hh]);
+          o[t] = mfma32<DT>(va, pb[st], o[t]);
+        }
       }
     }
+    if (kt + 1 < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
   }
 
   if (!row_ok) return;
@@ -249,8 +329,8 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(AttnArgs a, PoolArgs p,
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = 32 * t + 8 * a4 + 4 * hh;
       uint2 w;
-      w.x = pack2<DT>(o[t][4 * a4] * inv, o[t][4 * a4 + 1] * inv);
-      w.y = pack2<DT>(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
+      w.x = cvt2<DT>(o[t][4 * a4] * inv, o[t][4 * a4 + 1] * inv);
+      w.y = cvt2<DT>(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
       *reinterpret_cast<uint2*>(op + d) = w;
     }
   }
@@ -259,11 +339,11 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(AttnArgs a, PoolArgs p,
 template <int DT, int D>
 hipError_t launch_tile_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                          int num_tiles, hipStream_t s) {
-  const dim3 grid(num_tiles, p.num_kv_heads);
+  const dim3 grid(num_tiles * p.num_kv_heads);
   if (p.block_size == 16)
-    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 16>), grid, dim3(256), 0, s, a, p, lay);
+    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 16>), grid, dim3(256), 0, s, a, p, lay, num_tiles);
   else if (p.block_size == 32)
-    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 32>), grid, dim3(256), 0, s, a, p, lay);
+    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 32>), grid, dim3(256), 0, s, a, p, lay, num_tiles);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -279,6 +359,7 @@ bool tile_path_supported(const PoolArgs& p) {
 hipError_t launch_tile_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                                  int num_tiles, hipStream_t s) {
   if (num_tiles == 0) return hipSuccess;
+  if ((int64_t)num_tiles * p.num_kv_heads > 0x7fffffff) return hipErrorInvalidValue;
   if (p.dtype == DT_F16) {
     if (p.head_dim == 64) return launch_tile_d<DT_F16, 64>(a, p, lay, num_tiles, s);
     if (p.head_dim == 128) return launch_tile_d<DT_F16, 128>(a, p, lay, num_tiles, s);
