@@ -91,6 +91,24 @@ def cpu_baseline(w, target_s: float):
             "gflops": nflops / t_used / 1e9}
 
 
+def copy_calibration(steps: int) -> int:
+    """pa_copy_blocks over 4096 distinct block pairs of a 40 x 16 x 128 fp16
+    pool: each launch reads and writes exactly 2 x 4096 x 163840 bytes."""
+    import torch
+    from paged_kv_cache_block_amd import binding
+    nb, h, bs, d = 8192, 40, 16, 128
+    k = torch.zeros((nb, h, bs, d), dtype=torch.float16, device="cuda")
+    v = torch.zeros((nb, h, d, bs), dtype=torch.float16, device="cuda")
+    pairs = torch.stack([torch.arange(4096), torch.arange(4096, 8192)], 1).to(torch.int32).cuda()
+    for _ in range(steps):
+        binding.pa_copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    per_launch = 2 * 4096 * h * bs * d * 2
+    print(json.dumps({"copy_calibration": {"launches": steps, "read_bytes_per_launch": per_launch,
+                                           "write_bytes_per_launch": per_launch}}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +119,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run pa_copy_blocks over a known byte count (scales HBM counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -116,6 +136,8 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 3
+    if args.copy_calibration:
+        return copy_calibration(args.steps)
     t0 = time.time()
     w = config_workload(args.config, args.seed)
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)

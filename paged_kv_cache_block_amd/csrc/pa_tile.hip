@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
   const TileItem ti = reinterpret_cast<const TileItem*>(ws + lay.tiles)[item];
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int lane = tid & 63;
   const int col = lane & 31;
   const int hh = lane >> 5;
@@ -160,12 +160,30 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
     for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Per-thread parts of the tile loads.  K chunk j is key kt0 + ktok + KRP*j,
+  // head-dim chunk kdc; V chunk j is head-dim row vd + 32*j, keys
+  // kt0 + vkey .. +8.  Offsets are within a block's (block, head) slice.
+  constexpr int TPR = D / 8;            // 16-byte chunks per K row
+  constexpr int KRP = 256 / TPR;        // K rows per pass of the workgroup
+  const int ktok = tid / TPR;
+  const int kdc = tid % TPR;
+  const int vd = tid >> 3;
+  const int vkey = 8 * (tid & 7);
+  const uint64_t kstride = (uint64_t)Hkv * BS * D;     // elements per physical block
+  int kofs[KCH];
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) kofs[j] = ((g * BS + (ktok + KRP * j) % BS) * D) + kdc * 8;
+  int vofs[VCH];
+#pragma unroll
+  for (int j = 0; j < VCH; ++j) vofs[j] = ((g * D + vd + 32 * j) * BS) + vkey % BS;
+
   const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
   u32x4 kbuf[KCH], vbuf[VCH];
 
-  // The sequence's block ids, kTabWin at a time, clamped to the pool.  A
-  // 64-key tile never straddles two windows (kTabWin is a multiple of 64/BS).
+  // The sequence's block ids, kTabWin at a time, clamped to the pool (so
+  // every load below stays inside it).  A 64-key tile never straddles two
+  // windows (kTabWin is a multiple of 64/BS).
   int win = -1;
   auto ensure_window = [&](int kt) {
     const int w = (kt * kKeys / BS) / kTabWin;
@@ -176,64 +194,43 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
     __syncthreads();
     win = w;
   };
-  auto block_of = [&](int kt0, int rel) -> unsigned {
-    return btab[(kt0 + rel) / BS - win * kTabWin];
-  };
   auto load_tile = [&](int kt) {
     ensure_window(kt);
     const int kt0 = kt * kKeys;
+    const int b0 = kt0 / BS - win * kTabWin;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int idx = tid + 256 * j;
-      const int tok = idx / (D / 8);
-      const int dc = idx % (D / 8);
-      const int key = kt0 + tok;
-      if (key < kend) {
-        const unsigned blk = block_of(kt0, tok);
-        kbuf[j] = *reinterpret_cast<const u32x4*>(
-            kc + (((int64_t)blk * Hkv + g) * BS + key % BS) * D + dc * 8);
-      } else {
-        kbuf[j] = u32x4{0, 0, 0, 0};
-      }
+      const unsigned blk = btab[b0 + (ktok + KRP * j) / BS];
+      kbuf[j] = *reinterpret_cast<const u32x4*>(kc + blk * kstride + kofs[j]);
     }
+    const unsigned vblk = btab[b0 + vkey / BS];
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int idx = tid + 256 * j;
-      const int d = idx >> 3;
-      const int kc8 = idx & 7;
-      const int key0 = kt0 + kc8 * 8;
-      if (key0 < kend) {
-        const unsigned blk = block_of(kt0, kc8 * 8);
-        u32x4 v = *reinterpret_cast<const u32x4*>(
-            vc + (((int64_t)blk * Hkv + g) * D + d) * BS + key0 % BS);
-        if (key0 + 8 > kend) {       // unwritten slots may hold NaN
+    for (int j = 0; j < VCH; ++j)
+      vbuf[j] = *reinterpret_cast<const u32x4*>(vc + vblk * kstride + vofs[j]);
+    if (kt0 + kKeys > kend) {
+      // Tail tile: slots at or past kend may be unwritten (NaN).  Zero the V
+      // entries (a zero probability must not meet them); K rows there are
+      // masked to -inf before the softmax.  The empty asm keeps this a real
+      // branch instead of selects executed on every tile.
+      asm volatile("" ::: "memory");
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t x = v[w];
-            if (key0 + 2 * w >= kend) x &= 0xffff0000u;
-            if (key0 + 2 * w + 1 >= kend) x &= 0x0000ffffu;
-            v[w] = x;
-          }
+      for (int j = 0; j < VCH; ++j)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t x = vbuf[j][w];
+          if (kt0 + vkey + 2 * w >= kend) x &= 0xffff0000u;
+          if (kt0 + vkey + 2 * w + 1 >= kend) x &= 0x0000ffffu;
+          vbuf[j][w] = x;
         }
-        vbuf[j] = v;
-      } else {
-        vbuf[j] = u32x4{0, 0, 0, 0};
-      }
     }
   };
   auto store_tile = [&](int stage) {
-    uint16_t* kd = Ks + stage * KSTAGE;
-    uint16_t* vd = Vs + stage * VSTAGE;
+    uint16_t* kd = Ks + stage * KSTAGE + ktok * KROW + kdc * 8;
+    uint16_t* vd_ = Vs + stage * VSTAGE + vd * VROW + vkey;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int idx = tid + 256 * j;
-      *reinterpret_cast<u32x4*>(&kd[(idx / (D / 8)) * KROW + (idx % (D / 8)) * 8]) = kbuf[j];
-    }
+    for (int j = 0; j < KCH; ++j) *reinterpret_cast<u32x4*>(kd + KRP * j * KROW) = kbuf[j];
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int idx = tid + 256 * j;
-      *reinterpret_cast<u32x4*>(&vd[(idx >> 3) * VROW + (idx & 7) * 8]) = vbuf[j];
-    }
+    for (int j = 0; j < VCH; ++j) *reinterpret_cast<u32x4*>(vd_ + 32 * j * VROW) = vbuf[j];
   };
 
   const int ntiles = (kend + kKeys - 1) / kKeys;
@@ -263,11 +260,12 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
       }
       // Causal mask (a select), only where some key passes some row's limit.
       if (!wave_full || kt0 + kKeys - 1 > wfirst) {
+        const int lim = p_row - kt0 - 8 * hh;    // key kt0 + 32u + 16(e>>3) + 8hh + (e&7)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            if (kt0 + 32 * u + acc_key(e, hh) > p_row) sacc[u][e] = -INFINITY;
+            if (32 * u + 16 * (e >> 3) + (e & 7) > lim) sacc[u][e] = -INFINITY;
       }
       // Row max of this tile (raw scores), both lane halves.
       float mx = -INFINITY;
