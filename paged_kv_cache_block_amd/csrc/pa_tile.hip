@@ -267,28 +267,27 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
           for (int e = 0; e < 16; ++e)
             if (32 * u + 16 * (e >> 3) + (e & 7) > lim) sacc[u][e] = -INFINITY;
       }
-      // Row max of this tile (raw scores), both lane halves.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_cand = mx * c;
-      const bool raise = m_cand > m_run + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = raise ? m_cand : m_run;
-        const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 on the first raise
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) o[t] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float rs = 0.f;
-      u32x4 pb[4];
+      // Online softmax and P.V per 32-key half: while the VALU works on one
+      // half, the MFMAs of the other half's products are in flight.
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float m_cand = mx * c;
+        const bool raise = m_cand > m_run + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float m_new = raise ? m_cand : m_run;
+          const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 on the first raise
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float rs = 0.f;
+        u32x4 pb[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float pe = fast_exp2(fmaf(sacc[u][e], c, -m_use));
@@ -299,18 +298,18 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
         for (int v2 = 0; v2 < 2; ++v2)
 #pragma unroll
           for (int w = 0; w < 4; ++w)
-            pb[2 * u + v2][w] = cvt2<DT>(sacc[u][8 * v2 + 2 * w], sacc[u][8 * v2 + 2 * w + 1]);
-      }
-      rs += swap_halves(rs);
-      l_run += rs;
-      // O^T += V^T . P^T over 4 k-steps of 16 keys.
+            pb[v2][w] = cvt2<DT>(sacc[u][8 * v2 + 2 * w], sacc[u][8 * v2 + 2 * w + 1]);
+        rs += swap_halves(rs);
+        l_run += rs;
+        // O^T += V^T . P^T over the half's 2 k-steps of 16 keys.
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) {
+        for (int t = 0; t < NDT; ++t) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const u32x4 va = *reinterpret_cast<const u32x4*>(
-              &vs_[(32 * t + col) * VROW + 16 * st + 8 * hh]);
-          o[t] = mfma32<DT>(va, pb[st], o[t]);
+          for (int v2 = 0; v2 < 2; ++v2) {
+            const u32x4 va = *reinterpret_cast<const u32x4*>(
+                &vs_[(32 * t + col) * VROW + 32 * u + 16 * v2 + 8 * hh]);
+            o[t] = mfma32<DT>(va, pb[v2], o[t]);
+          }
         }
       }
     }
