@@ -207,8 +207,12 @@ __global__ __launch_bounds__(64) void row_attn_kernel(AttnArgs a, PoolArgs p, Wo
   }
 }
 
+// Merge the split states of one row: thread (h, d) owns one output element.
+// Split states are fetched eight at a time with independent loads, so a row
+// with many splits costs a few memory latencies rather than one per split.
 template <int DT>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, WorkspaceLayout lay, int D) {
+  constexpr int U = 8;
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
   const PlanCounts* pc = reinterpret_cast<const PlanCounts*>(ws + lay.counts);
   if ((int)blockIdx.x >= pc->combs) return;
@@ -218,21 +222,35 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, WorkspaceLayou
   const int h = e / D;
   const int d = e % D;
   if (h >= Hq || ci.row >= a.total_q || ci.pslot < 0 || ci.pslot + ci.nsplit > lay.cap_partials) return;
-  const float* po = reinterpret_cast<const float*>(ws + lay.part_o);
-  const float2* pm = reinterpret_cast<const float2*>(ws + lay.part_ml);
+  const float* po = reinterpret_cast<const float*>(ws + lay.part_o) + (int64_t)ci.pslot * Hq * D + h * D + d;
+  const float2* pm = reinterpret_cast<const float2*>(ws + lay.part_ml) + (int64_t)ci.pslot * Hq + h;
+  const int64_t so = (int64_t)Hq * D;   // stride between splits, in floats
   float mx = -INFINITY;
-  for (int k = 0; k < ci.nsplit; ++k) {
-    const float2 ml = pm[(int64_t)(ci.pslot + k) * Hq + h];
-    if (ml.y > 0.f) mx = fmaxf(mx, ml.x);
+  for (int k0 = 0; k0 < ci.nsplit; k0 += U) {
+    float2 ml[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ml[u] = k0 + u < ci.nsplit ? pm[(int64_t)(k0 + u) * Hq] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ml[u].y > 0.f) mx = fmaxf(mx, ml[u].x);
   }
   float lsum = 0.f, o = 0.f;
-  for (int k = 0; k < ci.nsplit; ++k) {
-    const int64_t slot = ci.pslot + k;
-    const float2 ml = pm[slot * Hq + h];
-    if (!(ml.y > 0.f)) continue;
-    const float w = fast_exp2(ml.x - mx);
-    lsum += w * ml.y;
-    o += w * po[(slot * Hq + h) * D + d];
+  for (int k0 = 0; k0 < ci.nsplit; k0 += U) {
+    float2 ml[U];
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = k0 + u < ci.nsplit;
+      ml[u] = in ? pm[(int64_t)(k0 + u) * Hq] : make_float2(-INFINITY, 0.f);
+      acc[u] = in ? po[(int64_t)(k0 + u) * so] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!(ml[u].y > 0.f)) continue;
+      const float w = fast_exp2(ml[u].x - mx);
+      lsum += w * ml[u].y;
+      o += w * acc[u];
+    }
   }
   const float v = o / lsum;
   const int64_t at = ((int64_t)ci.row * Hq + h) * D + d;
