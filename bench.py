@@ -55,6 +55,15 @@ def work_model(w):
     return m
 
 
+def blocks_unshared(w) -> bool:
+    """True when no physical block is read by two sequences of the batch --
+    what a caller's block manager knows from its reference counts."""
+    bs = w.block_size
+    used = [w.block_tables[s, :(int(L) + bs - 1) // bs] for s, L in enumerate(w.context_lens)]
+    ids = np.concatenate(used) if used else np.zeros(0, np.int32)
+    return np.unique(ids).size == ids.size
+
+
 def cpu_baseline(w, target_s: float):
     """The oracle, as it stands, on a bounded sample of sequences."""
     import oracle
@@ -141,7 +150,9 @@ def main(argv=None) -> int:
     t0 = time.time()
     w = config_workload(args.config, args.seed)
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
-    db = DeviceBatch(w, opt=binding.options(args.split))
+    unshared = blocks_unshared(w)
+    flags = binding.PA_FLAG_KV_UNSHARED if unshared else 0
+    db = DeviceBatch(w, opt=binding.options(args.split, 0, flags))
     db.write_history()
     torch.cuda.synchronize()
     model = work_model(w)
@@ -163,7 +174,7 @@ def main(argv=None) -> int:
         db.write_new()
         db.attention(opt=opt)
 
-    base_opt = binding.options(args.split)
+    base_opt = binding.options(args.split, 0, flags)
     for _ in range(args.warmup):
         run_step(base_opt)
     torch.cuda.synchronize()
@@ -173,7 +184,7 @@ def main(argv=None) -> int:
     dom_id = dict(kernels)[dominant]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
-    opts = [binding.options(args.split, 0, 0, dom_id, a, b) for a, b in evs]
+    opts = [binding.options(args.split, 0, flags, dom_id, a, b) for a, b in evs]
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -192,7 +203,7 @@ def main(argv=None) -> int:
             continue
         evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(K)]
-        opts2 = [binding.options(args.split, 0, 0, kid, a, b) for a, b in evs2]
+        opts2 = [binding.options(args.split, 0, flags, kid, a, b) for a, b in evs2]
         for i in range(K):
             run_step(opts2[i])
         torch.cuda.synchronize()
@@ -232,7 +243,7 @@ def main(argv=None) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "config": args.config, "seqs": w.num_seqs,
                    "query_rows": int(w.q.shape[0]), "new_tokens": int(w.k_new.shape[0]),
-                   "cow_pairs": int(w.cow_pairs.shape[0]),
+                   "cow_pairs": int(w.cow_pairs.shape[0]), "kv_unshared_hint": unshared,
                    "step_bytes": model["step_bytes"], "multi_token_flops": model["tile_flops"]},
         "roofline": roof,
         "kernels_ms": {k2: round(v, 5) for k2, v in per_kernel.items()},

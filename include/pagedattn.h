@@ -86,8 +86,14 @@ typedef struct {
   int32_t decode_split_tokens;
   /* Tokens per split of a multi-token request's context; 0 = no split. */
   int32_t prefill_split_tokens;
-  /* Bit 0: route every row through the vector-ALU row kernel (the MFMA
-   * multi-token kernel is skipped).  Other bits must be 0. */
+  /* Bit 0 (PA_FLAG_VECTOR_ALU): route every row through the vector-ALU row
+   * kernel (the MFMA kernels are skipped).
+   * Bit 1 (PA_FLAG_KV_UNSHARED): the caller asserts that no physical block
+   * is read by two sequences of this call (no reference-count sharing, no
+   * sub-requests over one table row).  Decode then streams K/V with
+   * non-temporal loads, which is faster when nothing is re-read and slower
+   * when blocks are shared; results are identical either way.
+   * Other bits must be 0. */
   int32_t flags;
   /* Profiling hook: when timed_kernel is one of PA_TIME_* and that kernel is
    * launched, timing_start / timing_end (caller-created hipEvent_t, may be
@@ -98,6 +104,7 @@ typedef struct {
 } pa_options;
 
 enum { PA_TIME_NONE = 0, PA_TIME_TILE = 1, PA_TIME_ROWS = 2, PA_TIME_COMBINE = 3 };
+enum { PA_FLAG_VECTOR_ALU = 1, PA_FLAG_KV_UNSHARED = 2 };
 
 /*
  * pa_write_kv -- slot-mapping scatter of new K/V into the pools.

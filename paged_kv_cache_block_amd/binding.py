@@ -35,6 +35,7 @@ class PaOptions(ctypes.Structure):
 
 
 PA_TIME_NONE, PA_TIME_TILE, PA_TIME_ROWS, PA_TIME_COMBINE = 0, 1, 2, 3
+PA_FLAG_VECTOR_ALU, PA_FLAG_KV_UNSHARED = 1, 2
 
 
 class PagedAttnError(RuntimeError):

@@ -76,7 +76,7 @@ int choose_split(const pa_options* opt, int64_t total_keys, int num_kv_heads) {
 }
 
 bool vector_all(const PoolArgs& p, const pa_options* opt) {
-  return (opt && (opt->flags & 1)) || !tile_path_supported(p);
+  return (opt && (opt->flags & PA_FLAG_VECTOR_ALU)) || !tile_path_supported(p);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -208,7 +208,8 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not supported", group);
   if (num_seqs < 0 || total_q < 0) return fail(PA_ERR_INVALID_ARG, "negative num_seqs or total_q");
-  if (opt && (opt->flags & ~1)) return fail(PA_ERR_INVALID_ARG, "unknown option flags");
+  if (opt && (opt->flags & ~(PA_FLAG_VECTOR_ALU | PA_FLAG_KV_UNSHARED)))
+    return fail(PA_ERR_INVALID_ARG, "unknown option flags");
   if (opt && (opt->decode_split_tokens < 0 || opt->prefill_split_tokens < 0))
     return fail(PA_ERR_INVALID_ARG, "negative split length");
   if (opt && (opt->timed_kernel < 0 || opt->timed_kernel > PA_TIME_COMBINE))
@@ -311,7 +312,8 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   if (n_rows > 0) {
     mark(PA_TIME_ROWS, opt ? opt->timing_start : nullptr);
     e = (!va && decode_mfma_supported(p, group))
-            ? launch_decode_mfma(a, p, lay, (int)n_rows, split, stream)
+            ? launch_decode_mfma(a, p, lay, (int)n_rows, split,
+                                 opt && (opt->flags & PA_FLAG_KV_UNSHARED), stream)
             : launch_row_attention(a, p, lay, (int)n_rows, split, stream);
     if (e != hipSuccess) return hip_fail(e, "row attention launch");
     mark(PA_TIME_ROWS, opt ? opt->timing_end : nullptr);

@@ -30,6 +30,22 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLazyRescale = 8.f;  // log2 headroom before the running max moves
+
+// Two floats to two packed 16-bit values, round to nearest even (hardware).
+template <int DT>
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  if constexpr (DT == DT_F16) {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -41,13 +57,20 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16-byte load; NT streams past the caches (data read once).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+
 template <int D>
 struct Stage {
   u32x4 k[2][D / 32];   // two 16-key tiles x (D/32) k-steps
   u32x4 v[D / 16];      // D/16 head-dim tiles, 8 keys each
 };
 
-template <int DT, int D, int BS>
+template <int DT, int D, int BS, bool NT>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
                                                          WorkspaceLayout lay, int split_tokens) {
   constexpr int KS = D / 32;
@@ -109,7 +132,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
       const int off = (c0 + kk) % BS;
       const uint16_t* kp = kc + (((int64_t)blk * Hkv + g) * BS + off) * D + 8 * grp;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) st.k[u][ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks)
+        st.k[u][ks] = ld16<NT>(kp + 32 * ks);
     }
     {
       const unsigned blk = (BS == 16 && vkey >= 16) ? b1 : b0;
@@ -117,7 +141,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
       const uint16_t* vp = vc + (((int64_t)blk * Hkv + g) * D + c16) * BS + off;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        st.v[dt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)16 * dt * BS);
+        st.v[dt] = ld16<NT>(vp + (int64_t)16 * dt * BS);
     }
   };
 
@@ -149,21 +173,27 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);           // finite: key c0 < t1
-    const float alpha = fast_exp2(m_run - m_new);
+    // The running max only moves when this step's max passes it by 2^8; the
+    // weights stay below 2^8 and most steps skip rescaling O.
+    if (mx > m_run + kLazyRescale) {               // per column (lane): may diverge
+      const float alpha = fast_exp2(m_run - mx);   // 0 on the first step
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m_run = mx;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sv[e] = fast_exp2(sv[e] - m_new);
+      sv[e] = fast_exp2(sv[e] - m_run);
       rs += sv[e];
     }
     rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+    l_run += rs;
     u32x4 pb;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) pb[w] = pack2<DT>(sv[2 * w], sv[2 * w + 1]);
+    for (int w = 0; w < 4; ++w) pb[w] = cvt2<DT>(sv[2 * w], sv[2 * w + 1]);
     if (tail) {
       // Slots at or past t1 may be unwritten (NaN); zero them, never multiply.
 #pragma unroll
@@ -178,10 +208,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
       }
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] *= alpha;
-      o[dt] = mfma16<DT>(st.v[dt], pb, o[dt]);
-    }
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma16<DT>(st.v[dt], pb, o[dt]);
   };
 
   Stage<D> sa, sb;
@@ -224,17 +251,24 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, bool NT>
 hipError_t launch_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay, int items,
                     int split, hipStream_t s) {
   const dim3 grid(items, p.num_kv_heads);
   if (p.block_size == 16)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 16>), grid, dim3(64), 0, s, a, p, lay, split);
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 16, NT>), grid, dim3(64), 0, s, a, p, lay, split);
   else if (p.block_size == 32)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 32>), grid, dim3(64), 0, s, a, p, lay, split);
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 32, NT>), grid, dim3(64), 0, s, a, p, lay, split);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_nt(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay, int items,
+                     int split, bool stream_kv, hipStream_t s) {
+  return stream_kv ? launch_d<DT, D, true>(a, p, lay, items, split, s)
+                   : launch_d<DT, D, false>(a, p, lay, items, split, s);
 }
 
 }  // namespace
@@ -245,14 +279,14 @@ bool decode_mfma_supported(const PoolArgs& p, int group) {
 }
 
 hipError_t launch_decode_mfma(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
-                              int num_items, int split_tokens, hipStream_t s) {
+                              int num_items, int split_tokens, bool stream_kv, hipStream_t s) {
   if (num_items == 0) return hipSuccess;
   if (p.dtype == DT_F16) {
-    if (p.head_dim == 64) return launch_d<DT_F16, 64>(a, p, lay, num_items, split_tokens, s);
-    if (p.head_dim == 128) return launch_d<DT_F16, 128>(a, p, lay, num_items, split_tokens, s);
+    if (p.head_dim == 64) return launch_nt<DT_F16, 64>(a, p, lay, num_items, split_tokens, stream_kv, s);
+    if (p.head_dim == 128) return launch_nt<DT_F16, 128>(a, p, lay, num_items, split_tokens, stream_kv, s);
   } else if (p.dtype == DT_BF16) {
-    if (p.head_dim == 64) return launch_d<DT_BF16, 64>(a, p, lay, num_items, split_tokens, s);
-    if (p.head_dim == 128) return launch_d<DT_BF16, 128>(a, p, lay, num_items, split_tokens, s);
+    if (p.head_dim == 64) return launch_nt<DT_BF16, 64>(a, p, lay, num_items, split_tokens, stream_kv, s);
+    if (p.head_dim == 128) return launch_nt<DT_BF16, 128>(a, p, lay, num_items, split_tokens, stream_kv, s);
   }
   return hipErrorInvalidValue;
 }

@@ -66,7 +66,7 @@ hipError_t launch_row_attention(const AttnArgs& a, const PoolArgs& p, const Work
                                 int num_items, int split_tokens, hipStream_t s);
 bool decode_mfma_supported(const PoolArgs& p, int group);
 hipError_t launch_decode_mfma(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
-                              int num_items, int split_tokens, hipStream_t s);
+                              int num_items, int split_tokens, bool stream_kv, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                           int num_combs, hipStream_t s);
 hipError_t launch_tile_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,

@@ -82,12 +82,13 @@ def test_write_and_copy_bit_exact(torch_cuda, cfg):
     assert np.array_equal(bits(gv), bits(v)), "V pool differs"
 
 
-@pytest.mark.parametrize("mode", ["default", "split64", "rows"])
+@pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_attention_small(torch_cuda, cfg, mode):
-    step = _step_mod()
     from paged_kv_cache_block_amd import binding
-    opt = {"default": None, "split64": binding.options(64), "rows": binding.options(0, 0, 1)}[mode]
+    opt = {"default": None, "split64": binding.options(64),
+           "rows": binding.options(0, 0, binding.PA_FLAG_VECTOR_ALU),
+           "stream": binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED)}[mode]
     w = small_workload(cfg)
     say("attention", w.name, mode)
     db = run_gpu(w, opt)
@@ -150,6 +151,17 @@ def test_shape_sweep(torch_cuda, shape):
     want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
                             w.num_kv_heads, w.dtype, w.scale)
     compare(db.out_numpy(), want, w.dtype, what=f"shape {shape}")
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_streaming_hint_is_bit_identical(torch_cuda, cfg):
+    """The no-sharing hint only changes the cache policy of the loads."""
+    from paged_kv_cache_block_amd import binding
+    w = small_workload(cfg)
+    say("stream hint", w.name)
+    a = run_gpu(w).out_numpy()
+    b = run_gpu(w, binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED)).out_numpy()
+    assert np.array_equal(bits(a), bits(b))
 
 
 def test_split_lengths_agree(torch_cuda):
