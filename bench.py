@@ -118,6 +118,38 @@ def copy_calibration(steps: int) -> int:
     return 0
 
 
+def hbm_reference() -> int:
+    """Reference HBM rates on this GPU, for context beside the kernel figures."""
+    import torch
+    from paged_kv_cache_block_amd import binding
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    x = torch.randn(1 << 30, dtype=torch.float16, device="cuda")      # 2 GiB
+    out = {"torch_sum_read_GBs": 2 * 2**30 / timed(lambda: x.sum(dtype=torch.float32)) / 1e6}
+    y = torch.empty_like(x)
+    out["torch_copy_read_write_GBs"] = 4 * 2**30 / timed(lambda: y.copy_(x)) / 1e6
+    del x, y
+    nb, h, bs, d = 8192, 40, 16, 128
+    k = torch.zeros((nb, h, bs, d), dtype=torch.float16, device="cuda")
+    v = torch.zeros((nb, h, d, bs), dtype=torch.float16, device="cuda")
+    pairs = torch.stack([torch.arange(4096), torch.arange(4096, 8192)], 1).to(torch.int32).cuda()
+    ms = timed(lambda: binding.pa_copy_blocks(k, v, pairs))
+    out["pa_copy_blocks_read_write_GBs"] = 2 * 2 * 4096 * h * bs * d * 2 / ms / 1e6
+    print(json.dumps({"hbm_reference": {k2: round(v2, 1) for k2, v2 in out.items()}}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +162,8 @@ def main(argv=None) -> int:
     ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks over a known byte count (scales HBM counters)")
+    ap.add_argument("--hbm-reference", action="store_true",
+                    help="only measure reference HBM rates (torch sum and copy, pa_copy_blocks)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -147,6 +181,8 @@ def main(argv=None) -> int:
         return 3
     if args.copy_calibration:
         return copy_calibration(args.steps)
+    if args.hbm_reference:
+        return hbm_reference()
     t0 = time.time()
     w = config_workload(args.config, args.seed)
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)

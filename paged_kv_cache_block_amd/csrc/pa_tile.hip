@@ -65,6 +65,18 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   }
 }
 
+// acc + the two packed 16-bit values of w (v_dot2 with a ones vector).
+template <int DT>
+__device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
+  if constexpr (DT == DT_F16) {
+    const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+  } else {
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+  }
+}
+
 // Key (within a 32-key half tile) held by accumulator element e of lane half hh.
 __device__ __forceinline__ int acc_key(int e, int hh) { return 16 * (e >> 3) + 8 * hh + (e & 7); }
 
@@ -286,19 +298,21 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
           m_run = m_new;
         }
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float rs = 0.f;
         u32x4 pb[2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pe = fast_exp2(fmaf(sacc[u][e], c, -m_use));
-          sacc[u][e] = pe;
-          rs += pe;
-        }
+        for (int e = 0; e < 16; ++e) sacc[u][e] = fast_exp2(fmaf(sacc[u][e], c, -m_use));
 #pragma unroll
         for (int v2 = 0; v2 < 2; ++v2)
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             pb[v2][w] = cvt2<DT>(sacc[u][8 * v2 + 2 * w], sacc[u][8 * v2 + 2 * w + 1]);
+        // Row sum of the rounded probabilities the MFMA consumes (packed dot
+        // products with ones), so O is normalised by exactly its own weights.
+        float rs = 0.f;
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) rs = dot2_ones<DT>(pb[v2][w], rs);
         rs += swap_halves(rs);
         l_run += rs;
         // O^T += V^T . P^T over the half's 2 k-steps of 16 keys.
