@@ -260,6 +260,12 @@ def main(argv=None) -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None, "kernel": "tile_attn_kernel",
                 "algorithmic_flops": model["tile_flops"], "avg_ms": round(dom_ms, 5)}
+    from paged_kv_cache_block_amd.profiling import traffic_record_for
+    rec = traffic_record_for(roof["kernel"], args.config) if args.split == 0 else None
+    if rec is not None:
+        roof["traffic"] = rec["fetch_bytes"] + rec["write_bytes"]
+        roof["traffic_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                "scaled by pa_copy_blocks over a known byte count")
     extra = {}
     if "tile" in per_kernel:
         extra["multi_token_tflops"] = round(model["tile_flops"] / (per_kernel["tile"] * 1e-3) / 1e12, 1)
