@@ -160,6 +160,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
+    ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 128, 256],
+                    help="rows per multi-token MFMA work item (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks over a known byte count (scales HBM counters)")
     ap.add_argument("--hbm-reference", action="store_true",
@@ -188,7 +190,7 @@ def main(argv=None) -> int:
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     unshared = blocks_unshared(w)
     flags = binding.PA_FLAG_KV_UNSHARED if unshared else 0
-    db = DeviceBatch(w, opt=binding.options(args.split, 0, flags))
+    db = DeviceBatch(w, opt=binding.options(args.split, 0, flags, prefill_tile_rows=args.tile_rows))
     db.write_history()
     torch.cuda.synchronize()
     model = work_model(w)
@@ -210,7 +212,7 @@ def main(argv=None) -> int:
         db.write_new()
         db.attention(opt=opt)
 
-    base_opt = binding.options(args.split, 0, flags)
+    base_opt = binding.options(args.split, 0, flags, prefill_tile_rows=args.tile_rows)
     for _ in range(args.warmup):
         run_step(base_opt)
     torch.cuda.synchronize()
@@ -220,7 +222,7 @@ def main(argv=None) -> int:
     dom_id = dict(kernels)[dominant]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
-    opts = [binding.options(args.split, 0, flags, dom_id, a, b) for a, b in evs]
+    opts = [binding.options(args.split, 0, flags, dom_id, a, b, args.tile_rows) for a, b in evs]
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -239,7 +241,7 @@ def main(argv=None) -> int:
             continue
         evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(K)]
-        opts2 = [binding.options(args.split, 0, flags, kid, a, b) for a, b in evs2]
+        opts2 = [binding.options(args.split, 0, flags, kid, a, b, args.tile_rows) for a, b in evs2]
         for i in range(K):
             run_step(opts2[i])
         torch.cuda.synchronize()
@@ -261,7 +263,8 @@ def main(argv=None) -> int:
                 "frac": round(achieved / peak, 4), "traffic": None, "kernel": "tile_attn_kernel",
                 "algorithmic_flops": model["tile_flops"], "avg_ms": round(dom_ms, 5)}
     from paged_kv_cache_block_amd.profiling import traffic_record_for
-    rec = traffic_record_for(roof["kernel"], args.config) if args.split == 0 else None
+    rec = (traffic_record_for(roof["kernel"], args.config)
+           if args.split == 0 and args.tile_rows == 0 else None)
     if rec is not None:
         roof["traffic"] = rec["fetch_bytes"] + rec["write_bytes"]
         roof["traffic_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "

@@ -101,6 +101,10 @@ typedef struct {
   int32_t timed_kernel;
   hipEvent_t timing_start;
   hipEvent_t timing_end;
+  /* Rows of (token, head) pairs per multi-token MFMA work item: 128 (4
+   * waves) or 256 (8 waves sharing each staged K/V tile); 0 = auto (256 when
+   * the batch has enough work items to fill the GPU). */
+  int32_t prefill_tile_rows;
 } pa_options;
 
 enum { PA_TIME_NONE = 0, PA_TIME_TILE = 1, PA_TIME_ROWS = 2, PA_TIME_COMBINE = 3 };

@@ -31,7 +31,8 @@ class PaCacheDesc(ctypes.Structure):
 class PaOptions(ctypes.Structure):
     _fields_ = [("decode_split_tokens", ctypes.c_int32), ("prefill_split_tokens", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("timed_kernel", ctypes.c_int32),
-                ("timing_start", ctypes.c_void_p), ("timing_end", ctypes.c_void_p)]
+                ("timing_start", ctypes.c_void_p), ("timing_end", ctypes.c_void_p),
+                ("prefill_tile_rows", ctypes.c_int32)]
 
 
 PA_TIME_NONE, PA_TIME_TILE, PA_TIME_ROWS, PA_TIME_COMBINE = 0, 1, 2, 3
@@ -101,7 +102,7 @@ def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> PaCacheDesc:
 
 
 def options(decode_split_tokens: int = 0, prefill_split_tokens: int = 0, flags: int = 0,
-            timed_kernel: int = 0, timing_start=None, timing_end=None):
+            timed_kernel: int = 0, timing_start=None, timing_end=None, prefill_tile_rows: int = 0):
     """``timing_start`` / ``timing_end`` are ``torch.cuda.Event(enable_timing=True)``
     objects (or raw hipEvent_t handles) recorded around ``timed_kernel``."""
     def handle(ev):
@@ -112,7 +113,7 @@ def options(decode_split_tokens: int = 0, prefill_split_tokens: int = 0, flags: 
             ev = ev.cuda_event
         return ev
     return PaOptions(decode_split_tokens, prefill_split_tokens, flags, timed_kernel,
-                     handle(timing_start), handle(timing_end))
+                     handle(timing_start), handle(timing_end), prefill_tile_rows)
 
 
 def pa_write_kv(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:

@@ -212,6 +212,9 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
     return fail(PA_ERR_INVALID_ARG, "unknown option flags");
   if (opt && (opt->decode_split_tokens < 0 || opt->prefill_split_tokens < 0))
     return fail(PA_ERR_INVALID_ARG, "negative split length");
+  if (opt && opt->prefill_tile_rows != 0 && opt->prefill_tile_rows != kTileRows &&
+      opt->prefill_tile_rows != kTileRowsWide)
+    return fail(PA_ERR_INVALID_ARG, "prefill_tile_rows must be 0, %d or %d", kTileRows, kTileRowsWide);
   if (opt && (opt->timed_kernel < 0 || opt->timed_kernel > PA_TIME_COMBINE))
     return fail(PA_ERR_INVALID_ARG, "unknown timed_kernel %d", opt->timed_kernel);
   if (num_seqs > 0 && (!context_lens_host || !query_start_loc_host))
@@ -274,11 +277,22 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
     for (int i = w.row_first; i < w.row_first + w.rows; ++i) total_keys += L - n + i + 1;
   }
   const int split = choose_split(opt, total_keys, p.num_kv_heads);
+  // Wide (256-row) multi-token work items when there are enough of them.
+  int tile_rows = kTileRows;
+  if (opt && opt->prefill_tile_rows) {
+    tile_rows = opt->prefill_tile_rows;
+  } else if (!va) {
+    int64_t wide = 0;
+    for (int s = 0; s < num_seqs; ++s)
+      wide += seq_work(query_start_loc_host[s + 1] - query_start_loc_host[s], 0, group,
+                       kTileRowsWide).tiles;
+    if (wide * p.num_kv_heads >= kWideTileMinGroups) tile_rows = kTileRowsWide;
+  }
   int64_t n_rows = 0, n_tiles = 0, n_combs = 0;
   for (int s = 0; s < num_seqs; ++s) {
     const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
     const int L = context_lens_host[s];
-    const SeqWork w = seq_work(n, va ? 1 : 0, group, kTileRows);
+    const SeqWork w = seq_work(n, va ? 1 : 0, group, tile_rows);
     for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
       const int ns = row_splits(L - n + i + 1, split);
       n_rows += ns;
@@ -291,7 +305,7 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   if (n_rows > 0x7fffffff || n_tiles > 0x7fffffff)
     return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
 
-  PlanParams pp{num_seqs, split, group, va ? 1 : 0,
+  PlanParams pp{num_seqs, split, group, va ? 1 : 0, tile_rows,
                 lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials};
   hipError_t e = launch_plan(context_lens, query_start_loc, pp, workspace, lay, stream);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
@@ -305,7 +319,7 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   };
   if (n_tiles > 0) {
     mark(PA_TIME_TILE, opt ? opt->timing_start : nullptr);
-    if ((e = launch_tile_attention(a, p, lay, (int)n_tiles, stream)) != hipSuccess)
+    if ((e = launch_tile_attention(a, p, lay, (int)n_tiles, tile_rows, stream)) != hipSuccess)
       return hip_fail(e, "multi-token attention launch");
     mark(PA_TIME_TILE, opt ? opt->timing_end : nullptr);
   }

@@ -10,8 +10,14 @@
 
 namespace pa {
 
-// Rows of packed (token, head) pairs per MFMA workgroup: 4 waves x 32 rows.
+// Rows of packed (token, head) pairs per MFMA workgroup: 4 waves x 32 rows,
+// or 8 waves x 32 rows for batches with enough tiles to fill the GPU.
 constexpr int kTileRows = 128;
+constexpr int kTileRowsWide = 256;
+// 256-row workgroups (8 waves sharing each staged K/V tile) issue half the
+// tile loads and LDS stores per MFMA; they pay off once a batch has enough of
+// them to keep every CU busy.
+constexpr int kWideTileMinGroups = 1024;
 // Keys per MFMA iteration.
 constexpr int kTileKeys = 32;
 // Automatic split length of single-row work: about kAutoTargetWaves
@@ -36,6 +42,7 @@ struct PlanParams {
   int split_tokens;   // keys per split of a row-kernel row
   int group;          // query heads per KV head
   int vector_all;     // 1: every row goes to the row kernel
+  int tile_rows;      // rows per MFMA multi-token work item
   int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
 };
 
@@ -70,7 +77,7 @@ hipError_t launch_decode_mfma(const AttnArgs& a, const PoolArgs& p, const Worksp
 hipError_t launch_combine(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                           int num_combs, hipStream_t s);
 hipError_t launch_tile_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
-                                 int num_tiles, hipStream_t s);
+                                 int num_tiles, int tile_rows, hipStream_t s);
 bool tile_path_supported(const PoolArgs& p);
 
 }  // namespace pa

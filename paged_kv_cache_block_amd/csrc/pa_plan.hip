@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   for (int s = s0; s < s1; ++s) {
     const int n = qsl[s + 1] - qsl[s];
     const int L = lens[s];
-    const SeqWork w = seq_work(n, pp.vector_all, pp.group, kTileRows);
+    const SeqWork w = seq_work(n, pp.vector_all, pp.group, pp.tile_rows);
     for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
       const int ns = row_splits(L - n + i + 1, pp.split_tokens);
       c[0] += ns;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   for (int s = s0; s < s1; ++s) {
     const int n = qsl[s + 1] - qsl[s];
     const int L = lens[s];
-    const SeqWork w = seq_work(n, pp.vector_all, pp.group, kTileRows);
+    const SeqWork w = seq_work(n, pp.vector_all, pp.group, pp.tile_rows);
     for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
       const int ns = row_splits(L - n + i + 1, pp.split_tokens);
       int32_t pslot = -1;

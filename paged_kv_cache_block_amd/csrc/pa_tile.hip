@@ -6,18 +6,20 @@
 // (融合因果掩码与内核实现): the causal mask is applied inside the kernel and
 // the score matrix is never materialised.
 //
-// Work item: one sequence, one KV head and a tile of 128 packed rows, where
-// row r is (new token r / G, query head g*G + r % G); all G query heads of a
-// KV head share each K/V tile.  Four wavefronts take 32 rows each.
+// Work item: one sequence, one KV head and a tile of 32 * NW packed rows
+// (NW = 4 or 8 wavefronts of 32 rows), where row r is (new token r / G,
+// query head g*G + r % G); all G query heads of a KV head share each K/V
+// tile.
 //
-// Keys go 64 per iteration through a two-stage LDS ring: while the waves
-// compute on one stage, every thread holds the next tile's K/V chunks in
-// registers and writes them to the other stage afterwards; one barrier per
-// iteration.  Each wave computes, with v_mfma_f32_32x32x16_{f16,bf16}:
-//   S^T[key][row] = K[key][:] . Q[row][:]           (2 x D/16 MFMAs)
+// Keys go 64 per iteration through a two-stage LDS ring fed from two sets of
+// registers: while the waves compute on one stage, the next tile waits in
+// registers for the other stage and the tile after it is in flight; one
+// barrier per iteration.  Each wave computes, per 32-key half, with
+// v_mfma_f32_32x32x16_{f16,bf16}:
+//   S^T[key][row] = K[key][:] . Q[row][:]           (D/16 MFMAs)
 //   online softmax per row (a row is one lane column of S^T, split over the
 //   two lane halves), causal mask from absolute key positions
-//   O^T[d][row]  += V^T[d][key] . P^T[key][row]      (D/32 x 4 MFMAs)
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row]      (D/32 x 2 MFMAs)
 // Working on the transposes keeps each row's statistics inside a lane pair
 // and lets both operands of the second product be read as 16-byte runs.
 // The K rows feeding S^T are permuted so that the eight keys a lane holds for
@@ -99,17 +101,24 @@ __device__ __forceinline__ int xcd_order(int bid, int n) {
   return xcd * per + min(xcd, rem) + pos;
 }
 
-template <int DT, int D, int BS>
-__global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs p,
-                                                          WorkspaceLayout lay, int num_tiles) {
+// NW = waves per workgroup (4 or 8), 32 rows each: the K/V tile staged in
+// LDS serves 32 * NW rows, so larger workgroups issue fewer loads and LDS
+// stores per MFMA.  Two waves per SIMD either way.
+template <int DT, int D, int BS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, PoolArgs p,
+                                                                   WorkspaceLayout lay, int num_tiles) {
+  constexpr int CB = 1;             // 32-row column blocks per wave
+  constexpr int NT = 64 * NW;       // threads per workgroup
   constexpr int KS = D / 16;        // k-steps of the QK product
   constexpr int NDT = D / 32;       // 32-row head-dim tiles of O^T
   constexpr int KROW = D + 8;       // LDS row stride of K (elements), padded
   constexpr int VROW = kKeys + 8;   // LDS row stride of V^T (elements), padded
-  constexpr int KCH = kKeys * D / 8 / 256;   // 16-byte K chunks per thread per tile
-  constexpr int VCH = D * kKeys / 8 / 256;   // 16-byte V chunks per thread per tile
+  constexpr int KCH = kKeys * D / 8 / NT;    // 16-byte K chunks per thread per tile
+  constexpr int VCH = D * kKeys / 8 / NT;    // 16-byte V chunks per thread per tile
   constexpr int KSTAGE = kKeys * KROW;
   constexpr int VSTAGE = D * VROW;
+  constexpr int WROWS = 32 * CB;    // rows per wave
+  constexpr int TROWS = NW * WROWS; // rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VSTAGE];
   __shared__ unsigned btab[kTabWin];
@@ -135,48 +144,61 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
   const int n = a.qsl[s + 1] - q0;
   const int L = a.context_lens[s];
   const int R = n * G;
-  const int r0 = ti.tile * kTileRows;
+  const int r0 = ti.tile * TROWS;
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
   const unsigned nb_max = p.num_blocks - 1;
   const int tb_max = a.max_blocks - 1;
   const float c = a.scale_log2;
 
-  // This lane's row.
-  const int r = r0 + 32 * wv + col;
-  const bool row_ok = r < R && q0 + r / G < a.total_q;
-  const int qi = row_ok ? r / G : 0;
-  const int hq = g * G + (row_ok ? r % G : 0);
-  const int p_row = row_ok ? L - n + qi : -1;
+  // This lane's rows: one per column block.
+  const int wr0 = r0 + WROWS * wv;            // first row of the wave
+  bool row_ok[CB];
+  int qi[CB], hq[CB], p_row[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int r = wr0 + 32 * cb + col;
+    row_ok[cb] = r < R && q0 + r / G < a.total_q;
+    qi[cb] = row_ok[cb] ? r / G : 0;
+    hq[cb] = g * G + (row_ok[cb] ? r % G : 0);
+    p_row[cb] = row_ok[cb] ? L - n + qi[cb] : -1;
+  }
   // Key ranges: the workgroup's and this wave's (rows ascend, so the last
   // row of a range has the largest causal limit, the first the smallest).
-  const int kend = L - n + (min(R, r0 + kTileRows) - 1) / G + 1;
-  const bool wave_on = r0 + 32 * wv < R;
-  const bool wave_full = r0 + 32 * wv + 32 <= R;
-  const int wend = wave_on ? L - n + (min(R, r0 + 32 * wv + 32) - 1) / G + 1 : 0;
-  const int wfirst = wave_on ? L - n + (r0 + 32 * wv) / G : 0;
+  const int kend = L - n + (min(R, r0 + TROWS) - 1) / G + 1;
+  const bool wave_on = wr0 < R;
+  const bool wave_full = wr0 + WROWS <= R;
+  const int wfirst = wave_on ? L - n + wr0 / G : 0;
 
-  // Q^T operand of the QK product: lane (col, hh) holds Q[row col][16ks+8hh .. +8].
-  u32x4 qreg[KS];
-  {
+  // Q^T operands of the QK product: lane (col, hh) of column block cb holds
+  // Q[row][16ks+8hh .. +8].
+  u32x4 qreg[CB][KS];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(q0 + qi) * Hq + hq) * D + 8 * hh;
+                         ((int64_t)(q0 + qi[cb]) * Hq + hq[cb]) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      qreg[cb][ks] = row_ok[cb] ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 o[NDT];
+  f32x16 o[CB][NDT];
+  float m_run[CB], l_run[CB];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t)
+  for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[cb][t][e] = 0.f;
+    m_run[cb] = -INFINITY;
+    l_run[cb] = 0.f;
+  }
 
   // Per-thread parts of the tile loads.  K chunk j is key kt0 + ktok + KRP*j,
   // head-dim chunk kdc; V chunk j is head-dim row vd + 32*j, keys
   // kt0 + vkey .. +8.  Offsets are within a block's (block, head) slice.
   constexpr int TPR = D / 8;            // 16-byte chunks per K row
-  constexpr int KRP = 256 / TPR;        // K rows per pass of the workgroup
+  constexpr int KRP = NT / TPR;         // K rows per pass of the workgroup
+  constexpr int VRP = NT / 8;           // V^T rows per pass of the workgroup
   const int ktok = tid / TPR;
   const int kdc = tid % TPR;
   const int vd = tid >> 3;
@@ -187,11 +209,15 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
   for (int j = 0; j < KCH; ++j) kofs[j] = ((g * BS + (ktok + KRP * j) % BS) * D) + kdc * 8;
   int vofs[VCH];
 #pragma unroll
-  for (int j = 0; j < VCH; ++j) vofs[j] = ((g * D + vd + 32 * j) * BS) + vkey % BS;
+  for (int j = 0; j < VCH; ++j) vofs[j] = ((g * D + vd + VRP * j) * BS) + vkey % BS;
 
   const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
-  u32x4 kbuf[KCH], vbuf[VCH];
+  // One tile's K/V chunks of this thread, held in registers between the
+  // global load and the LDS store.
+  struct Buf {
+    u32x4 k[KCH], v[VCH];
+  };
 
   // The sequence's block ids, kTabWin at a time, clamped to the pool (so
   // every load below stays inside it).  A 64-key tile never straddles two
@@ -201,163 +227,210 @@ __global__ __launch_bounds__(256, 2) void tile_attn_kernel(AttnArgs a, PoolArgs 
     const int w = (kt * kKeys / BS) / kTabWin;
     if (w == win) return;
     __syncthreads();
-    for (int i = tid; i < kTabWin; i += 256)
+    for (int i = tid; i < kTabWin; i += NT)
       btab[i] = min((unsigned)bt[min(w * kTabWin + i, tb_max)], nb_max);
     __syncthreads();
     win = w;
   };
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](Buf& b, int kt) {
     ensure_window(kt);
     const int kt0 = kt * kKeys;
     const int b0 = kt0 / BS - win * kTabWin;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
       const unsigned blk = btab[b0 + (ktok + KRP * j) / BS];
-      kbuf[j] = *reinterpret_cast<const u32x4*>(kc + blk * kstride + kofs[j]);
+      b.k[j] = *reinterpret_cast<const u32x4*>(kc + blk * kstride + kofs[j]);
     }
     const unsigned vblk = btab[b0 + vkey / BS];
 #pragma unroll
     for (int j = 0; j < VCH; ++j)
-      vbuf[j] = *reinterpret_cast<const u32x4*>(vc + vblk * kstride + vofs[j]);
+      b.v[j] = *reinterpret_cast<const u32x4*>(vc + vblk * kstride + vofs[j]);
+  };
+  // Tail tile: slots at or past kend may be unwritten (NaN).  Zero the V
+  // entries (a zero probability must not meet them); K rows there are masked
+  // to -inf before the softmax.  Runs just before the tile is stored.
+  auto zero_tail = [&](Buf& b, int kt) {
+    const int kt0 = kt * kKeys;
     if (kt0 + kKeys > kend) {
-      // Tail tile: slots at or past kend may be unwritten (NaN).  Zero the V
-      // entries (a zero probability must not meet them); K rows there are
-      // masked to -inf before the softmax.  The empty asm keeps this a real
-      // branch instead of selects executed on every tile.
-      asm volatile("" ::: "memory");
+      asm volatile("" ::: "memory");   // keep this a real branch, not selects
 #pragma unroll
       for (int j = 0; j < VCH; ++j)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          uint32_t x = vbuf[j][w];
+          uint32_t x = b.v[j][w];
           if (kt0 + vkey + 2 * w >= kend) x &= 0xffff0000u;
           if (kt0 + vkey + 2 * w + 1 >= kend) x &= 0x0000ffffu;
-          vbuf[j][w] = x;
+          b.v[j][w] = x;
         }
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](const Buf& b, int stage) {
     uint16_t* kd = Ks + stage * KSTAGE + ktok * KROW + kdc * 8;
     uint16_t* vd_ = Vs + stage * VSTAGE + vd * VROW + vkey;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) *reinterpret_cast<u32x4*>(kd + KRP * j * KROW) = kbuf[j];
+    for (int j = 0; j < KCH; ++j) *reinterpret_cast<u32x4*>(kd + KRP * j * KROW) = b.k[j];
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) *reinterpret_cast<u32x4*>(vd_ + 32 * j * VROW) = vbuf[j];
+    for (int j = 0; j < VCH; ++j) *reinterpret_cast<u32x4*>(vd_ + VRP * j * VROW) = b.v[j];
   };
 
   const int ntiles = (kend + kKeys - 1) / kKeys;
   const int krow = row_key(col);
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+  const int wend = wave_on ? L - n + (min(R, wr0 + WROWS) - 1) / G + 1 : 0;
+  auto compute = [&](int kt, int stage) {
     const int kt0 = kt * kKeys;
     if (wave_on && kt0 < wend) {
       const uint16_t* ks_ = Ks + stage * KSTAGE;
       const uint16_t* vs_ = Vs + stage * VSTAGE;
-      // S^T = K . Q^T for keys kt0 + [0, 32) and kt0 + [32, 64).
-      f32x16 sacc[2];
+      // One 32-key half at a time: S^T = K . Q^T (each K operand feeds every
+      // column block), causal mask, online softmax, O^T += V^T . P^T.
+      const bool need_mask = !wave_full || kt0 + kKeys - 1 > wfirst;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        f32x16 sacc[CB];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[u][e] = 0.f;
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[cb][e] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const u32x4 ka = *reinterpret_cast<const u32x4*>(
               &ks_[(32 * u + krow) * KROW + 16 * ks + 8 * hh]);
-          sacc[u] = mfma32<DT>(ka, qreg[ks], sacc[u]);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) sacc[cb] = mfma32<DT>(ka, qreg[cb][ks], sacc[cb]);
         }
-      }
-      // Causal mask (a select), only where some key passes some row's limit.
-      if (!wave_full || kt0 + kKeys - 1 > wfirst) {
-        const int lim = p_row - kt0 - 8 * hh;    // key kt0 + 32u + 16(e>>3) + 8hh + (e&7)
+        // Causal mask (a select), only where some key passes some row's limit.
+        if (need_mask) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+          for (int cb = 0; cb < CB; ++cb) {
+            const int lim = p_row[cb] - kt0 - 32 * u - 8 * hh;   // key kt0 + 32u + 16(e>>3) + 8hh + (e&7)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (32 * u + 16 * (e >> 3) + (e & 7) > lim) sacc[u][e] = -INFINITY;
-      }
-      // Online softmax and P.V per 32-key half: while the VALU works on one
-      // half, the MFMAs of the other half's products are in flight.
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_cand = mx * c;
-        const bool raise = m_cand > m_run + kLazyRescale;
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-          const float m_new = raise ? m_cand : m_run;
-          const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 on the first raise
-          l_run *= alpha;
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) o[t] *= alpha;
-          m_run = m_new;
+            for (int e = 0; e < 16; ++e)
+              if (16 * (e >> 3) + (e & 7) > lim) sacc[cb][e] = -INFINITY;
+          }
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        u32x4 pb[2];
+        bool raise[CB];
+        float m_cand[CB];
+        bool any = false;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[u][e] = fast_exp2(fmaf(sacc[u][e], c, -m_use));
+        for (int cb = 0; cb < CB; ++cb) {
+          float mx = -INFINITY;
 #pragma unroll
-        for (int v2 = 0; v2 < 2; ++v2)
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[cb][e]);
+          mx = fmaxf(mx, swap_halves(mx));
+          m_cand[cb] = mx * c;
+          raise[cb] = m_cand[cb] > m_run[cb] + kLazyRescale;
+          any = any || raise[cb];
+        }
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-            pb[v2][w] = cvt2<DT>(sacc[u][8 * v2 + 2 * w], sacc[u][8 * v2 + 2 * w + 1]);
-        // Row sum of the rounded probabilities the MFMA consumes (packed dot
-        // products with ones), so O is normalised by exactly its own weights.
-        float rs = 0.f;
+          for (int cb = 0; cb < CB; ++cb) {
+            const float m_new = raise[cb] ? m_cand[cb] : m_run[cb];
+            const float alpha = raise[cb] ? fast_exp2(m_run[cb] - m_new) : 1.f;   // 0 on the first raise
+            l_run[cb] *= alpha;
 #pragma unroll
-        for (int v2 = 0; v2 < 2; ++v2)
+            for (int t = 0; t < NDT; ++t) o[cb][t] *= alpha;
+            m_run[cb] = m_new;
+          }
+        }
+        u32x4 pb[CB][2];
 #pragma unroll
-          for (int w = 0; w < 4; ++w) rs = dot2_ones<DT>(pb[v2][w], rs);
-        rs += swap_halves(rs);
-        l_run += rs;
-        // O^T += V^T . P^T over the half's 2 k-steps of 16 keys.
+        for (int cb = 0; cb < CB; ++cb) {
+          const float m_use = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[cb][e] = fast_exp2(fmaf(sacc[cb][e], c, -m_use));
+          float rs = 0.f;
+#pragma unroll
+          for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              pb[cb][v2][w] = cvt2<DT>(sacc[cb][8 * v2 + 2 * w], sacc[cb][8 * v2 + 2 * w + 1]);
+              // Row sum of the rounded probabilities the MFMA consumes, so O
+              // is normalised by exactly its own weights.
+              rs = dot2_ones<DT>(pb[cb][v2][w], rs);
+            }
+          rs += swap_halves(rs);
+          l_run[cb] += rs;
+        }
+        // O^T += V^T . P^T over the half's 2 k-steps of 16 keys; each V
+        // operand feeds every column block.
 #pragma unroll
         for (int t = 0; t < NDT; ++t) {
 #pragma unroll
           for (int v2 = 0; v2 < 2; ++v2) {
             const u32x4 va = *reinterpret_cast<const u32x4*>(
                 &vs_[(32 * t + col) * VROW + 32 * u + 16 * v2 + 8 * hh]);
-            o[t] = mfma32<DT>(va, pb[v2], o[t]);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) o[cb][t] = mfma32<DT>(va, pb[cb][v2], o[cb][t]);
           }
         }
       }
     }
-    if (kt + 1 < ntiles) store_tile(stage ^ 1);
+  };
+
+  // Two LDS stages and two register sets: while tile kt is computed from one
+  // stage, tile kt+1 waits in registers for the other stage and tile kt+2 is
+  // in flight, so every load has two iterations to arrive.  Past the last
+  // tile, loads and stores repeat the last tile into an idle stage.
+  const int last = ntiles - 1;
+  Buf ba, bb;
+  load_tile(ba, 0);
+  zero_tail(ba, 0);
+  store_tile(ba, 0);
+  load_tile(ba, min(1, last));
+  load_tile(bb, min(2, last));
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    compute(kt, 0);
+    zero_tail(ba, min(kt + 1, last));
+    store_tile(ba, 1);
+    load_tile(ba, min(kt + 3, last));
+    __syncthreads();
+    if (kt + 1 >= ntiles) break;
+    compute(kt + 1, 1);
+    zero_tail(bb, min(kt + 2, last));
+    store_tile(bb, 0);
+    load_tile(bb, min(kt + 4, last));
     __syncthreads();
   }
 
-  if (!row_ok) return;
-  const float inv = 1.f / l_run;
-  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q0 + qi) * Hq + hq) * D;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
+  for (int cb = 0; cb < CB; ++cb) {
+    if (!row_ok[cb]) continue;
+    const float inv = 1.f / l_run[cb];
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q0 + qi[cb]) * Hq + hq[cb]) * D;
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int d = 32 * t + 8 * a4 + 4 * hh;
-      uint2 w;
-      w.x = cvt2<DT>(o[t][4 * a4] * inv, o[t][4 * a4 + 1] * inv);
-      w.y = cvt2<DT>(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d) = w;
+    for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * t + 8 * a4 + 4 * hh;
+        uint2 w;
+        w.x = cvt2<DT>(o[cb][t][4 * a4] * inv, o[cb][t][4 * a4 + 1] * inv);
+        w.y = cvt2<DT>(o[cb][t][4 * a4 + 2] * inv, o[cb][t][4 * a4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + d) = w;
+      }
     }
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, int NW>
 hipError_t launch_tile_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                          int num_tiles, hipStream_t s) {
   const dim3 grid(num_tiles * p.num_kv_heads);
   if (p.block_size == 16)
-    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 16>), grid, dim3(256), 0, s, a, p, lay, num_tiles);
+    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 16, NW>), grid, dim3(64 * NW), 0, s, a, p, lay, num_tiles);
   else if (p.block_size == 32)
-    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 32>), grid, dim3(256), 0, s, a, p, lay, num_tiles);
+    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 32, NW>), grid, dim3(64 * NW), 0, s, a, p, lay, num_tiles);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_tile_cb(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
+                          int num_tiles, int tile_rows, hipStream_t s) {
+  if (tile_rows == 128) return launch_tile_d<DT, D, 4>(a, p, lay, num_tiles, s);
+  if (tile_rows == 256) return launch_tile_d<DT, D, 8>(a, p, lay, num_tiles, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -368,15 +441,15 @@ bool tile_path_supported(const PoolArgs& p) {
 }
 
 hipError_t launch_tile_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
-                                 int num_tiles, hipStream_t s) {
+                                 int num_tiles, int tile_rows, hipStream_t s) {
   if (num_tiles == 0) return hipSuccess;
   if ((int64_t)num_tiles * p.num_kv_heads > 0x7fffffff) return hipErrorInvalidValue;
   if (p.dtype == DT_F16) {
-    if (p.head_dim == 64) return launch_tile_d<DT_F16, 64>(a, p, lay, num_tiles, s);
-    if (p.head_dim == 128) return launch_tile_d<DT_F16, 128>(a, p, lay, num_tiles, s);
+    if (p.head_dim == 64) return launch_tile_cb<DT_F16, 64>(a, p, lay, num_tiles, tile_rows, s);
+    if (p.head_dim == 128) return launch_tile_cb<DT_F16, 128>(a, p, lay, num_tiles, tile_rows, s);
   } else if (p.dtype == DT_BF16) {
-    if (p.head_dim == 64) return launch_tile_d<DT_BF16, 64>(a, p, lay, num_tiles, s);
-    if (p.head_dim == 128) return launch_tile_d<DT_BF16, 128>(a, p, lay, num_tiles, s);
+    if (p.head_dim == 64) return launch_tile_cb<DT_BF16, 64>(a, p, lay, num_tiles, tile_rows, s);
+    if (p.head_dim == 128) return launch_tile_cb<DT_BF16, 128>(a, p, lay, num_tiles, tile_rows, s);
   }
   return hipErrorInvalidValue;
 }

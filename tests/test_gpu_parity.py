@@ -82,13 +82,15 @@ def test_write_and_copy_bit_exact(torch_cuda, cfg):
     assert np.array_equal(bits(gv), bits(v)), "V pool differs"
 
 
-@pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream"])
+@pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream", "tile128", "tile256"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_attention_small(torch_cuda, cfg, mode):
     from paged_kv_cache_block_amd import binding
     opt = {"default": None, "split64": binding.options(64),
            "rows": binding.options(0, 0, binding.PA_FLAG_VECTOR_ALU),
-           "stream": binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED)}[mode]
+           "stream": binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED),
+           "tile128": binding.options(prefill_tile_rows=128),
+           "tile256": binding.options(prefill_tile_rows=256)}[mode]
     w = small_workload(cfg)
     say("attention", w.name, mode)
     db = run_gpu(w, opt)
@@ -142,15 +144,17 @@ SHAPES = [  # (dtype, H_q, H_kv, D, block_size)
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
 def test_shape_sweep(torch_cuda, shape):
+    from paged_kv_cache_block_amd import binding
     dtype, hq, hkv, d, bs = shape
     seqs = [(0, 1, 1), (47, 1, 1), (130, 1, 1), (0, 19, 1), (70, 45, 1), (5, 2, 1), (200, 1, 1)]
     w = build_batch(f"sweep {shape}", dtype, hq, hkv, d, bs, 512, seqs, 21)
-    say("shape", shape)
-    db = run_gpu(w)
     k, v = oracle_step(w)
     want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
                             w.num_kv_heads, w.dtype, w.scale)
-    compare(db.out_numpy(), want, w.dtype, what=f"shape {shape}")
+    for rows in (128, 256):
+        say("shape", shape, "tile rows", rows)
+        db = run_gpu(w, binding.options(prefill_tile_rows=rows))
+        compare(db.out_numpy(), want, w.dtype, what=f"shape {shape} tile rows {rows}")
 
 
 @pytest.mark.parametrize("cfg", [2, 5])
