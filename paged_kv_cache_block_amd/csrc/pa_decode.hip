@@ -171,8 +171,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
         sv[4 * u + i] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor_max<32>(xor_max<16>(mx));
     // The running max only moves when this step's max passes it by 2^8; the
     // weights stay below 2^8 and most steps skip rescaling O.
     if (mx > m_run + kLazyRescale) {               // per column (lane): may diverge
@@ -188,8 +187,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
       sv[e] = fast_exp2(sv[e] - m_run);
       rs += sv[e];
     }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
+    rs = xor_sum<32>(xor_sum<16>(rs));
     l_run += rs;
     u32x4 pb;
 #pragma unroll

@@ -84,6 +84,35 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x and its copy in lane l ^ M (M = 16 or 32), by v_permlane16_swap /
+// v_permlane32_swap: a VALU op, where a shuffle would be an LDS round trip.
+// Each lane receives its own value in one result and its partner's in the
+// other, so a symmetric combine of the two needs no select.
+template <int M>
+__device__ __forceinline__ void xor_pair(float x, float& p, float& q) {
+  static_assert(M == 16 || M == 32, "lane distance");
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    p = __uint_as_float(r[0]);
+    q = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    p = __uint_as_float(r[0]);
+    q = __uint_as_float(r[1]);
+  }
+}
+template <int M> __device__ __forceinline__ float xor_max(float x) {
+  float p, q;
+  xor_pair<M>(x, p, q);
+  return fmaxf(p, q);
+}
+template <int M> __device__ __forceinline__ float xor_sum(float x) {
+  float p, q;
+  xor_pair<M>(x, p, q);
+  return p + q;
+}
+
 // ---- workspace plan records ------------------------------------------------
 // One vector-ALU work item: a query row (seq, i) and one split of its keys.
 struct RowItem {

@@ -89,9 +89,6 @@ __device__ __forceinline__ int row_key(int r) {
   return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
 }
 
-// The other lane half's copy of x (lanes l and l ^ 32).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
-
 // Logical work index of this workgroup: consecutive logical indices share
 // K/V, and each XCD (workgroups dispatched round-robin over 8) gets one
 // contiguous range of them.
@@ -107,7 +104,6 @@ __device__ __forceinline__ int xcd_order(int bid, int n) {
 template <int DT, int D, int BS, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, PoolArgs p,
                                                                    WorkspaceLayout lay, int num_tiles) {
-  constexpr int CB = 1;             // 32-row column blocks per wave
   constexpr int NT = 64 * NW;       // threads per workgroup
   constexpr int KS = D / 16;        // k-steps of the QK product
   constexpr int NDT = D / 32;       // 32-row head-dim tiles of O^T
@@ -117,8 +113,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   constexpr int VCH = D * kKeys / 8 / NT;    // 16-byte V chunks per thread per tile
   constexpr int KSTAGE = kKeys * KROW;
   constexpr int VSTAGE = D * VROW;
-  constexpr int WROWS = 32 * CB;    // rows per wave
-  constexpr int TROWS = NW * WROWS; // rows per workgroup
+  constexpr int TROWS = 32 * NW;    // rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VSTAGE];
   __shared__ unsigned btab[kTabWin];
@@ -150,48 +145,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   const int tb_max = a.max_blocks - 1;
   const float c = a.scale_log2;
 
-  // This lane's rows: one per column block.
-  const int wr0 = r0 + WROWS * wv;            // first row of the wave
-  bool row_ok[CB];
-  int qi[CB], hq[CB], p_row[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int r = wr0 + 32 * cb + col;
-    row_ok[cb] = r < R && q0 + r / G < a.total_q;
-    qi[cb] = row_ok[cb] ? r / G : 0;
-    hq[cb] = g * G + (row_ok[cb] ? r % G : 0);
-    p_row[cb] = row_ok[cb] ? L - n + qi[cb] : -1;
-  }
+  // This lane's row.
+  const int wr0 = r0 + 32 * wv;               // first row of the wave
+  const int r = wr0 + col;
+  const bool row_ok = r < R && q0 + r / G < a.total_q;
+  const int qi = row_ok ? r / G : 0;
+  const int hq = g * G + (row_ok ? r % G : 0);
+  const int p_row = row_ok ? L - n + qi : -1;
   // Key ranges: the workgroup's and this wave's (rows ascend, so the last
   // row of a range has the largest causal limit, the first the smallest).
   const int kend = L - n + (min(R, r0 + TROWS) - 1) / G + 1;
   const bool wave_on = wr0 < R;
-  const bool wave_full = wr0 + WROWS <= R;
+  const bool wave_full = wr0 + 32 <= R;
   const int wfirst = wave_on ? L - n + wr0 / G : 0;
 
-  // Q^T operands of the QK product: lane (col, hh) of column block cb holds
-  // Q[row][16ks+8hh .. +8].
-  u32x4 qreg[CB][KS];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(q0 + qi[cb]) * Hq + hq[cb]) * D + 8 * hh;
+  // Q^T operands of the QK product: lane (col, hh) holds Q[row][16ks+8hh .. +8].
+  u32x4 qreg[KS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + qi) * Hq + hq) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qreg[cb][ks] = row_ok[cb] ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 o[CB][NDT];
-  float m_run[CB], l_run[CB];
+  f32x16 o[NDT];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
+  for (int t = 0; t < NDT; ++t)
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[cb][t][e] = 0.f;
-    m_run[cb] = -INFINITY;
-    l_run[cb] = 0.f;
-  }
+    for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
   // Per-thread parts of the tile loads.  K chunk j is key kt0 + ktok + KRP*j,
   // head-dim chunk kdc; V chunk j is head-dim row vd + 32*j, keys
@@ -275,94 +257,87 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
 
   const int ntiles = (kend + kKeys - 1) / kKeys;
   const int krow = row_key(col);
-  const int wend = wave_on ? L - n + (min(R, wr0 + WROWS) - 1) / G + 1 : 0;
+  const int wend = wave_on ? L - n + (min(R, wr0 + 32) - 1) / G + 1 : 0;
+  // LDS operand reads of one 32-key half: K rows for S^T, V^T rows for O^T.
+  // They are issued ahead of the MFMAs that consume them (the V^T of a half
+  // and the K of the next half before the half's softmax), so their latency
+  // hides behind that vector work.
+  auto read_k = [&](const uint16_t* ks_, int u, u32x4 (&kop)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kop[ks] = *reinterpret_cast<const u32x4*>(&ks_[(32 * u + krow) * KROW + 16 * ks + 8 * hh]);
+  };
+  auto read_v = [&](const uint16_t* vs_, int u, u32x4 (&vop)[NDT][2]) {
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int v2 = 0; v2 < 2; ++v2)
+        vop[t][v2] = *reinterpret_cast<const u32x4*>(&vs_[(32 * t + col) * VROW + 32 * u + 16 * v2 + 8 * hh]);
+  };
   auto compute = [&](int kt, int stage) {
     const int kt0 = kt * kKeys;
     if (wave_on && kt0 < wend) {
       const uint16_t* ks_ = Ks + stage * KSTAGE;
       const uint16_t* vs_ = Vs + stage * VSTAGE;
-      // One 32-key half at a time: S^T = K . Q^T (each K operand feeds every
-      // column block), causal mask, online softmax, O^T += V^T . P^T.
+      // One 32-key half at a time: S^T = K . Q^T, causal mask, online
+      // softmax, O^T += V^T . P^T.
       const bool need_mask = !wave_full || kt0 + kKeys - 1 > wfirst;
+      u32x4 kop[KS];
+      read_k(ks_, 0, kop);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        f32x16 sacc[CB];
+        if (u == 1 && NW != 8) read_k(ks_, 1, kop);
+        f32x16 sacc;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) sacc[cb][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(
-              &ks_[(32 * u + krow) * KROW + 16 * ks + 8 * hh]);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) sacc[cb] = mfma32<DT>(ka, qreg[cb][ks], sacc[cb]);
-        }
+        for (int ks = 0; ks < KS; ++ks) sacc = mfma32<DT>(kop[ks], qreg[ks], sacc);
+        u32x4 vop[NDT][2];
+        read_v(vs_, u, vop);
+        // (With 4-wave workgroups the register sets of the tile loads leave
+        // no room to hold the next half's K as well.)
+        if (u == 0 && NW == 8) read_k(ks_, 1, kop);
         // Causal mask (a select), only where some key passes some row's limit.
         if (need_mask) {
+          const int lim = p_row - kt0 - 32 * u - 8 * hh;   // key kt0 + 32u + 16(e>>3) + 8hh + (e&7)
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const int lim = p_row[cb] - kt0 - 32 * u - 8 * hh;   // key kt0 + 32u + 16(e>>3) + 8hh + (e&7)
+          for (int e = 0; e < 16; ++e)
+            if (16 * (e >> 3) + (e & 7) > lim) sacc[e] = -INFINITY;
+        }
+        float mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (16 * (e >> 3) + (e & 7) > lim) sacc[cb][e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+        const float m_cand = xor_max<32>(mx) * c;
+        const bool raise = m_cand > m_run + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float m_new = raise ? m_cand : m_run;
+          const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 on the first raise
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[e] = fast_exp2(fmaf(sacc[e], c, -m_use));
+        u32x4 pb[2];
+        float rs = 0.f;
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pb[v2][w] = cvt2<DT>(sacc[8 * v2 + 2 * w], sacc[8 * v2 + 2 * w + 1]);
+            // Row sum of the rounded probabilities the MFMA consumes, so O
+            // is normalised by exactly its own weights.
+            rs = dot2_ones<DT>(pb[v2][w], rs);
           }
-        }
-        bool raise[CB];
-        float m_cand[CB];
-        bool any = false;
+        l_run += xor_sum<32>(rs);
+        // O^T += V^T . P^T over the half's 2 k-steps of 16 keys, the
+        // independent accumulators back to back.
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          float mx = -INFINITY;
+        for (int v2 = 0; v2 < 2; ++v2)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[cb][e]);
-          mx = fmaxf(mx, swap_halves(mx));
-          m_cand[cb] = mx * c;
-          raise[cb] = m_cand[cb] > m_run[cb] + kLazyRescale;
-          any = any || raise[cb];
-        }
-        if (__builtin_amdgcn_ballot_w64(any) != 0) {
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const float m_new = raise[cb] ? m_cand[cb] : m_run[cb];
-            const float alpha = raise[cb] ? fast_exp2(m_run[cb] - m_new) : 1.f;   // 0 on the first raise
-            l_run[cb] *= alpha;
-#pragma unroll
-            for (int t = 0; t < NDT; ++t) o[cb][t] *= alpha;
-            m_run[cb] = m_new;
-          }
-        }
-        u32x4 pb[CB][2];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const float m_use = m_run[cb] == -INFINITY ? 0.f : m_run[cb];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sacc[cb][e] = fast_exp2(fmaf(sacc[cb][e], c, -m_use));
-          float rs = 0.f;
-#pragma unroll
-          for (int v2 = 0; v2 < 2; ++v2)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              pb[cb][v2][w] = cvt2<DT>(sacc[cb][8 * v2 + 2 * w], sacc[cb][8 * v2 + 2 * w + 1]);
-              // Row sum of the rounded probabilities the MFMA consumes, so O
-              // is normalised by exactly its own weights.
-              rs = dot2_ones<DT>(pb[cb][v2][w], rs);
-            }
-          rs += swap_halves(rs);
-          l_run[cb] += rs;
-        }
-        // O^T += V^T . P^T over the half's 2 k-steps of 16 keys; each V
-        // operand feeds every column block.
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-#pragma unroll
-          for (int v2 = 0; v2 < 2; ++v2) {
-            const u32x4 va = *reinterpret_cast<const u32x4*>(
-                &vs_[(32 * t + col) * VROW + 32 * u + 16 * v2 + 8 * hh]);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) o[cb][t] = mfma32<DT>(va, pb[cb][v2], o[cb][t]);
-          }
-        }
+          for (int t = 0; t < NDT; ++t) o[t] = mfma32<DT>(vop[t][v2], pb[v2], o[t]);
       }
     }
   };
@@ -393,21 +368,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
     __syncthreads();
   }
 
+  if (!row_ok) return;
+  const float inv = 1.f / l_run;
+  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q0 + qi) * Hq + hq) * D;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    if (!row_ok[cb]) continue;
-    const float inv = 1.f / l_run[cb];
-    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q0 + qi[cb]) * Hq + hq[cb]) * D;
+  for (int t = 0; t < NDT; ++t) {
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d = 32 * t + 8 * a4 + 4 * hh;
-        uint2 w;
-        w.x = cvt2<DT>(o[cb][t][4 * a4] * inv, o[cb][t][4 * a4 + 1] * inv);
-        w.y = cvt2<DT>(o[cb][t][4 * a4 + 2] * inv, o[cb][t][4 * a4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d) = w;
-      }
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = 32 * t + 8 * a4 + 4 * hh;
+      uint2 w;
+      w.x = cvt2<DT>(o[t][4 * a4] * inv, o[t][4 * a4 + 1] * inv);
+      w.y = cvt2<DT>(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = w;
     }
   }
 }
