@@ -11,11 +11,11 @@
 // query head g*G + r % G); all G query heads of a KV head share each K/V
 // tile.
 //
-// Keys go 64 per iteration through a two-stage LDS ring fed from two sets of
-// registers: while the waves compute on one stage, the next tile waits in
-// registers for the other stage and the tile after it is in flight; one
-// barrier per iteration.  Each wave computes, per 32-key half, with
-// v_mfma_f32_32x32x16_{f16,bf16}:
+// Keys go 64 (4 waves) or 128 (8 waves) per iteration through a two-stage
+// LDS ring fed from registers: while the waves compute on one stage, the
+// next tile waits in registers for the other stage (with 64-key tiles the
+// tile after it is in flight as well); one barrier per iteration.  Each wave
+// computes, per 32-key half, with v_mfma_f32_32x32x16_{f16,bf16}:
 //   S^T[key][row] = K[key][:] . Q[row][:]           (D/16 MFMAs)
 //   online softmax per row (a row is one lane column of S^T, split over the
 //   two lane halves), causal mask from absolute key positions
@@ -25,7 +25,8 @@
 // The K rows feeding S^T are permuted so that the eight keys a lane holds for
 // each P^T operand are consecutive, which is what the V^T operand reads.
 // The running max is only raised (and O rescaled) when a row's max grows by
-// more than 2^8, so most iterations skip the rescale.
+// more than 2^8, so most iterations skip the rescale.  The LDS operands of a
+// half are read before its softmax, so their latency hides behind it.
 // Workgroups are numbered so that the tiles sharing one (sequence, KV head)
 // run on one XCD and reuse its L2.
 
@@ -41,7 +42,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKeys = 64;          // keys per iteration
 constexpr int kTabWin = 256;       // block-table entries staged in LDS at a time
 constexpr float kLazyRescale = 8.f;  // log2 headroom before the running max moves
 
@@ -108,6 +108,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   constexpr int KS = D / 16;        // k-steps of the QK product
   constexpr int NDT = D / 32;       // 32-row head-dim tiles of O^T
   constexpr int KROW = D + 8;       // LDS row stride of K (elements), padded
+  // Keys per iteration: 128 for 8 waves (one register set of loads in
+  // flight), 64 for 4 waves (two sets).
+  constexpr int kKeys = NW == 8 ? 128 : 64;
+  constexpr int NH = kKeys / 32;    // 32-key halves per tile
   constexpr int VROW = kKeys + 8;   // LDS row stride of V^T (elements), padded
   constexpr int KCH = kKeys * D / 8 / NT;    // 16-byte K chunks per thread per tile
   constexpr int VCH = D * kKeys / 8 / NT;    // 16-byte V chunks per thread per tile
@@ -180,11 +184,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   // kt0 + vkey .. +8.  Offsets are within a block's (block, head) slice.
   constexpr int TPR = D / 8;            // 16-byte chunks per K row
   constexpr int KRP = NT / TPR;         // K rows per pass of the workgroup
-  constexpr int VRP = NT / 8;           // V^T rows per pass of the workgroup
+  constexpr int CPR = kKeys / 8;        // 16-byte chunks per V^T row of a tile
+  constexpr int VRP = NT / CPR;         // V^T rows per pass of the workgroup
   const int ktok = tid / TPR;
   const int kdc = tid % TPR;
-  const int vd = tid >> 3;
-  const int vkey = 8 * (tid & 7);
+  const int vd = tid / CPR;
+  const int vkey = 8 * (tid % CPR);
   const uint64_t kstride = (uint64_t)Hkv * BS * D;     // elements per physical block
   int kofs[KCH];
 #pragma unroll
@@ -202,8 +207,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   };
 
   // The sequence's block ids, kTabWin at a time, clamped to the pool (so
-  // every load below stays inside it).  A 64-key tile never straddles two
-  // windows (kTabWin is a multiple of 64/BS).
+  // every load below stays inside it).  A tile never straddles two windows
+  // (kTabWin is a multiple of kKeys / BS).
   int win = -1;
   auto ensure_window = [&](int kt) {
     const int w = (kt * kKeys / BS) / kTabWin;
@@ -285,8 +290,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
       u32x4 kop[KS];
       read_k(ks_, 0, kop);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (u == 1 && NW != 8) read_k(ks_, 1, kop);
+      for (int u = 0; u < NH; ++u) {
+        if (u > 0 && NW != 8) read_k(ks_, u, kop);
         f32x16 sacc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
         read_v(vs_, u, vop);
         // (With 4-wave workgroups the register sets of the tile loads leave
         // no room to hold the next half's K as well.)
-        if (u == 0 && NW == 8) read_k(ks_, 1, kop);
+        if (u + 1 < NH && NW == 8) read_k(ks_, u + 1, kop);
         // Causal mask (a select), only where some key passes some row's limit.
         if (need_mask) {
           const int lim = p_row - kt0 - 32 * u - 8 * hh;   // key kt0 + 32u + 16(e>>3) + 8hh + (e&7)
@@ -342,30 +347,54 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
     }
   };
 
-  // Two LDS stages and two register sets: while tile kt is computed from one
-  // stage, tile kt+1 waits in registers for the other stage and tile kt+2 is
-  // in flight, so every load has two iterations to arrive.  Past the last
-  // tile, loads and stores repeat the last tile into an idle stage.
+  // Two LDS stages: while tile kt is computed from one stage, tile kt+1
+  // waits in registers for the other.  With 64-key tiles a second register
+  // set keeps tile kt+2 in flight as well, so every load has two 64-key
+  // iterations to arrive; a 128-key iteration is long enough on its own.
+  // Past the last tile, loads and stores repeat the last tile into an idle
+  // stage.
   const int last = ntiles - 1;
-  Buf ba, bb;
-  load_tile(ba, 0);
-  zero_tail(ba, 0);
-  store_tile(ba, 0);
-  load_tile(ba, min(1, last));
-  load_tile(bb, min(2, last));
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    compute(kt, 0);
-    zero_tail(ba, min(kt + 1, last));
-    store_tile(ba, 1);
-    load_tile(ba, min(kt + 3, last));
+  if constexpr (NW == 8) {
+    Buf ba;
+    load_tile(ba, 0);
+    zero_tail(ba, 0);
+    store_tile(ba, 0);
+    load_tile(ba, min(1, last));
     __syncthreads();
-    if (kt + 1 >= ntiles) break;
-    compute(kt + 1, 1);
-    zero_tail(bb, min(kt + 2, last));
-    store_tile(bb, 0);
-    load_tile(bb, min(kt + 4, last));
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      compute(kt, 0);
+      zero_tail(ba, min(kt + 1, last));
+      store_tile(ba, 1);
+      load_tile(ba, min(kt + 2, last));
+      __syncthreads();
+      if (kt + 1 >= ntiles) break;
+      compute(kt + 1, 1);
+      zero_tail(ba, min(kt + 2, last));
+      store_tile(ba, 0);
+      load_tile(ba, min(kt + 3, last));
+      __syncthreads();
+    }
+  } else {
+    Buf ba, bb;
+    load_tile(ba, 0);
+    zero_tail(ba, 0);
+    store_tile(ba, 0);
+    load_tile(ba, min(1, last));
+    load_tile(bb, min(2, last));
     __syncthreads();
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      compute(kt, 0);
+      zero_tail(ba, min(kt + 1, last));
+      store_tile(ba, 1);
+      load_tile(ba, min(kt + 3, last));
+      __syncthreads();
+      if (kt + 1 >= ntiles) break;
+      compute(kt + 1, 1);
+      zero_tail(bb, min(kt + 2, last));
+      store_tile(bb, 0);
+      load_tile(bb, min(kt + 4, last));
+      __syncthreads();
+    }
   }
 
   if (!row_ok) return;
