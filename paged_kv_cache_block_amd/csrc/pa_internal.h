@@ -18,8 +18,6 @@ constexpr int kTileRowsWide = 256;
 // tile loads and LDS stores per MFMA; they pay off once a batch has enough of
 // them to keep every CU busy.
 constexpr int kWideTileMinGroups = 1024;
-// Keys per MFMA iteration.
-constexpr int kTileKeys = 32;
 // Automatic split length of single-row work: about kAutoTargetWaves
 // wavefronts over the whole batch, clamped to [kMinAutoSplit, kMaxAutoSplit]
 // keys and rounded to a multiple of 64.
