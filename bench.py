@@ -150,6 +150,31 @@ def hbm_reference() -> int:
     return 0
 
 
+def mfma_reference() -> int:
+    """Reference bf16 matrix-core rate on this GPU: a large dense torch GEMM
+    (hipBLASLt), for context beside the multi-token kernel's TFLOP/s."""
+    import torch
+
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"mfma_reference": {"torch_bf16_gemm_8192_TFLOPs": round(2 * n**3 / ms / 1e9, 1)}}),
+          flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +191,8 @@ def main(argv=None) -> int:
                     help="only run pa_copy_blocks over a known byte count (scales HBM counters)")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only measure reference HBM rates (torch sum and copy, pa_copy_blocks)")
+    ap.add_argument("--mfma-reference", action="store_true",
+                    help="time a large bf16 torch GEMM as a matrix-core reference rate, then exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -185,6 +212,8 @@ def main(argv=None) -> int:
         return copy_calibration(args.steps)
     if args.hbm_reference:
         return hbm_reference()
+    if args.mfma_reference:
+        return mfma_reference()
     t0 = time.time()
     w = config_workload(args.config, args.seed)
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
