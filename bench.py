@@ -175,6 +175,65 @@ def mfma_reference() -> int:
     return 0
 
 
+def chunk_cost(args) -> int:
+    """Attention time of one 32-token chunk after 0..32K cached tokens (and of
+    16 such chunks after up to 8K), on the long-mix head shape (64 query / 8 KV
+    heads of 128, bf16, block size 32): the table a recomputation cost model
+    interpolates.  Each context is timed without and with a key split sized to
+    give the GPU at least 256 workgroups."""
+    import torch
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.chunkcost import ChunkCostProfile
+    from paged_kv_cache_block_amd.step import DeviceBatch
+    from workloads import build_batch
+
+    chunk, hq, hkv, d, bs = 32, 64, 8, 128, 32
+    contexts = [0, 256, 1024, 2048, 4096, 8192, 16384, 32768]
+    reps = max(args.steps, 5)
+    rows = []
+    for batch, ctxs in ((1, contexts), (16, contexts[:6])):
+        for split_mode in ("none", "split"):
+            times = []
+            for ctx in ctxs:
+                L = ctx + chunk
+                nb = batch * ((L + bs - 1) // bs) + 8
+                w = build_batch(f"chunk {chunk} after {ctx}", "bf16", hq, hkv, d, bs, nb,
+                                [(ctx, chunk, 1)] * batch, 4242 + ctx)
+                psplit = 0
+                if split_mode == "split":
+                    items = batch * hkv           # one 256-row tile per chunk and KV head
+                    want = max(1, -(-256 // items))
+                    psplit = max(128, -(-L // want))
+                opt = binding.options(0, psplit, binding.PA_FLAG_KV_UNSHARED, prefill_tile_rows=256)
+                db = DeviceBatch(w, opt=opt)
+                db.write_history()
+                db.write_new()
+                torch.cuda.synchronize()
+                for _ in range(3):
+                    db.attention()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    db.attention()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / reps * 1e3
+                flops = 4 * d * hq * batch * (chunk * ctx + chunk * (chunk + 1) // 2)
+                times.append(us)
+                line = {"chunk_cost": {"chunk": chunk, "context": ctx, "batch": batch,
+                                       "prefill_split": psplit, "us": round(us, 2),
+                                       "us_per_chunk": round(us / batch, 2),
+                                       "tflops": round(flops / us / 1e6, 1)}}
+                rows.append(line)
+                print(json.dumps(line), flush=True)
+                del db
+            prof = ChunkCostProfile(chunk, ctxs, [t / batch for t in times],
+                                    {"batch": batch, "split": split_mode, "heads": [hq, hkv, d],
+                                     "dtype": "bf16", "block_size": bs})
+            print(json.dumps({"chunk_cost_profile": prof.to_dict()}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,12 +244,16 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
+    ap.add_argument("--prefill-split", type=int, default=0,
+                    help="keys per split of a multi-token context (0 = no split)")
     ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 128, 256],
                     help="rows per multi-token MFMA work item (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks over a known byte count (scales HBM counters)")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only measure reference HBM rates (torch sum and copy, pa_copy_blocks)")
+    ap.add_argument("--chunk-cost", action="store_true",
+                    help="time one 32-token chunk (and 16 of them) after 0..32K cached tokens, then exit")
     ap.add_argument("--mfma-reference", action="store_true",
                     help="time a large bf16 torch GEMM as a matrix-core reference rate, then exit")
     args = ap.parse_args(argv)
@@ -214,12 +277,14 @@ def main(argv=None) -> int:
         return hbm_reference()
     if args.mfma_reference:
         return mfma_reference()
+    if args.chunk_cost:
+        return chunk_cost(args)
     t0 = time.time()
     w = config_workload(args.config, args.seed)
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     unshared = blocks_unshared(w)
     flags = binding.PA_FLAG_KV_UNSHARED if unshared else 0
-    db = DeviceBatch(w, opt=binding.options(args.split, 0, flags, prefill_tile_rows=args.tile_rows))
+    db = DeviceBatch(w, opt=binding.options(args.split, args.prefill_split, flags, prefill_tile_rows=args.tile_rows))
     db.write_history()
     torch.cuda.synchronize()
     model = work_model(w)
@@ -241,7 +306,7 @@ def main(argv=None) -> int:
         db.write_new()
         db.attention(opt=opt)
 
-    base_opt = binding.options(args.split, 0, flags, prefill_tile_rows=args.tile_rows)
+    base_opt = binding.options(args.split, args.prefill_split, flags, prefill_tile_rows=args.tile_rows)
     for _ in range(args.warmup):
         run_step(base_opt)
     torch.cuda.synchronize()
@@ -251,7 +316,7 @@ def main(argv=None) -> int:
     dom_id = dict(kernels)[dominant]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
-    opts = [binding.options(args.split, 0, flags, dom_id, a, b, args.tile_rows) for a, b in evs]
+    opts = [binding.options(args.split, args.prefill_split, flags, dom_id, a, b, args.tile_rows) for a, b in evs]
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -270,7 +335,7 @@ def main(argv=None) -> int:
             continue
         evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(K)]
-        opts2 = [binding.options(args.split, 0, flags, kid, a, b, args.tile_rows) for a, b in evs2]
+        opts2 = [binding.options(args.split, args.prefill_split, flags, kid, a, b, args.tile_rows) for a, b in evs2]
         for i in range(K):
             run_step(opts2[i])
         torch.cuda.synchronize()
@@ -293,7 +358,7 @@ def main(argv=None) -> int:
                 "algorithmic_flops": model["tile_flops"], "avg_ms": round(dom_ms, 5)}
     from paged_kv_cache_block_amd.profiling import traffic_record_for
     rec = (traffic_record_for(roof["kernel"], args.config)
-           if args.split == 0 and args.tile_rows == 0 else None)
+           if args.split == 0 and args.tile_rows == 0 and args.prefill_split == 0 else None)
     if rec is not None:
         roof["traffic"] = rec["fetch_bytes"] + rec["write_bytes"]
         roof["traffic_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "

@@ -84,7 +84,11 @@ typedef struct {
    * Rounded up to a multiple of 64.  Each split yields a partial softmax
    * state that a combine kernel merges. */
   int32_t decode_split_tokens;
-  /* Tokens per split of a multi-token request's context; 0 = no split. */
+  /* Keys per split of a multi-token request's context, rounded up to a
+   * multiple of 128; 0 = no split.  Each (tile of rows, split) is a separate
+   * work item; a new token whose causal range spans several splits gets one
+   * partial softmax state per split, merged by the combine kernel (more
+   * parallelism for few, long requests).  The workspace size depends on it. */
   int32_t prefill_split_tokens;
   /* Bit 0 (PA_FLAG_VECTOR_ALU): route every row through the vector-ALU row
    * kernel (the MFMA kernels are skipped).

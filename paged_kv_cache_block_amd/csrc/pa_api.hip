@@ -75,6 +75,13 @@ int choose_split(const pa_options* opt, int64_t total_keys, int num_kv_heads) {
   return (int)std::min<int64_t>(kMaxAutoSplit, std::max<int64_t>(kMinAutoSplit, want));
 }
 
+// Keys per split of a multi-token sequence: the option rounded up to a whole
+// number of 128-key MFMA tiles; 0 = no split.
+int prefill_split(const pa_options* opt) {
+  if (!opt || opt->prefill_split_tokens <= 0) return 0;
+  return (opt->prefill_split_tokens + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum * kPrefillSplitQuantum;
+}
+
 bool vector_all(const PoolArgs& p, const pa_options* opt) {
   return (opt && (opt->flags & PA_FLAG_VECTOR_ALU)) || !tile_path_supported(p);
 }
@@ -100,6 +107,15 @@ WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q
   w.cap_combs = row_rows;
   w.cap_partials = w.cap_rows;
   w.cap_tiles = va ? 0 : ((int64_t)total_q * group + kTileRows - 1) / kTileRows + num_seqs;
+  const int ps = prefill_split(opt);
+  if (!va && ps > 0) {
+    // Every tile has at most key_splits(max_len) splits; every new token at
+    // most that many partial slots and one combine item.
+    const int64_t ks = key_splits(std::max(max_len, 1), ps);
+    w.cap_tiles *= ks;
+    w.cap_partials += (int64_t)total_q * ks;
+    w.cap_combs += total_q;
+  }
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(PlanCounts));
   w.rows = off;   off = align256(off + sizeof(RowItem) * (size_t)w.cap_rows);
@@ -288,7 +304,8 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
                        kTileRowsWide).tiles;
     if (wide * p.num_kv_heads >= kWideTileMinGroups) tile_rows = kTileRowsWide;
   }
-  int64_t n_rows = 0, n_tiles = 0, n_combs = 0;
+  const int psplit = va ? 0 : prefill_split(opt);
+  int64_t n_rows = 0, n_tiles = 0, n_combs = 0, n_partials = 0;
   for (int s = 0; s < num_seqs; ++s) {
     const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
     const int L = context_lens_host[s];
@@ -296,22 +313,29 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
     for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
       const int ns = row_splits(L - n + i + 1, split);
       n_rows += ns;
-      if (ns > 1) n_combs += 1;
+      if (ns > 1) {
+        n_combs += 1;
+        n_partials += ns;
+      }
     }
-    n_tiles += w.tiles;
+    const TileWork tw = tile_work(n, L, group, tile_rows, w.tiles, psplit);
+    n_tiles += tw.items;
+    n_combs += tw.combs;
+    n_partials += tw.slots;
   }
-  if (n_rows > lay.cap_rows || n_tiles > lay.cap_tiles || n_combs > lay.cap_combs)
+  if (n_rows > lay.cap_rows || n_tiles > lay.cap_tiles || n_combs > lay.cap_combs ||
+      n_partials > lay.cap_partials)
     return fail(PA_ERR_WORKSPACE, "plan exceeds workspace capacity");
   if (n_rows > 0x7fffffff || n_tiles > 0x7fffffff)
     return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
 
-  PlanParams pp{num_seqs, split, group, va ? 1 : 0, tile_rows,
+  PlanParams pp{num_seqs, split, group, va ? 1 : 0, tile_rows, psplit,
                 lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials};
   hipError_t e = launch_plan(context_lens, query_start_loc, pp, workspace, lay, stream);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
 
   AttnArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
-             max_blocks_per_seq, num_q_heads, total_q, scale * kLog2e, workspace};
+             max_blocks_per_seq, num_q_heads, total_q, scale * kLog2e, workspace, psplit};
   // Optional events around one kernel, recorded on `stream` (profiling hook).
   const int timed = opt ? opt->timed_kernel : 0;
   auto mark = [&](int which, hipEvent_t ev) {

@@ -121,10 +121,13 @@ struct RowItem {
   int32_t split;   // split index
   int32_t pslot;   // first partial slot of the row, or -1 if it has one split
 };
-// One MFMA work item: a tile of packed (token, head) rows of one sequence.
+// One MFMA work item: a tile of packed (token, head) rows of one sequence,
+// and one split of its keys.
 struct TileItem {
   int32_t seq;
   int32_t tile;
+  int32_t split;   // key split index
+  int32_t pslot;   // partial slot of the sequence's first token, or -1 (keys not split)
 };
 // One combine item: a row whose splits must be merged.
 struct CombItem {
@@ -164,6 +167,45 @@ __host__ __device__ inline SeqWork seq_work(int n, int vector_all, int group, in
 __host__ __device__ inline int row_splits(int keys, int split_tokens) {
   if (keys <= split_tokens) return 1;
   return (keys + split_tokens - 1) / split_tokens;
+}
+
+// Key splits of the multi-token path: split k covers keys
+// [k * split_tokens, (k + 1) * split_tokens); split_tokens = 0 means one.
+__host__ __device__ inline int key_splits(int keys, int split_tokens) {
+  if (split_tokens <= 0 || keys <= split_tokens) return 1;
+  return (keys + split_tokens - 1) / split_tokens;
+}
+
+// Keys visible to tile t of a sequence with n new tokens and context L
+// (exclusive end: one past the causal limit of the tile's last row).
+__host__ __device__ inline int tile_key_end(int n, int L, int group, int tile_rows, int t) {
+  const int R = n * group;
+  const int last = (t + 1) * tile_rows < R ? (t + 1) * tile_rows : R;
+  return L - n + (last - 1) / group + 1;
+}
+
+// Multi-token work of one sequence under a key split: tile items (one per
+// tile and split that holds a key of the tile), tokens whose splits need a
+// combine, and partial slots (n x splits of the whole context, token-major).
+struct TileWork {
+  int32_t items, combs, slots;
+};
+__host__ __device__ inline TileWork tile_work(int n, int L, int group, int tile_rows, int tiles,
+                                              int split_tokens) {
+  TileWork w{0, 0, 0};
+  if (tiles == 0) return w;
+  const int ns = key_splits(L, split_tokens);
+  if (ns == 1) {
+    w.items = tiles;
+    return w;
+  }
+  for (int t = 0; t < tiles; ++t)
+    w.items += key_splits(tile_key_end(n, L, group, tile_rows, t), split_tokens);
+  // Token i sees L - n + i + 1 keys: more than one split from i0 on.
+  const int i0 = split_tokens - (L - n) > 0 ? split_tokens - (L - n) : 0;
+  w.combs = n > i0 ? n - i0 : 0;
+  w.slots = n * ns;
+  return w;
 }
 
 }  // namespace pa

@@ -22,6 +22,9 @@ constexpr int kWideTileMinGroups = 1024;
 // wavefronts over the whole batch, clamped to [kMinAutoSplit, kMaxAutoSplit]
 // keys and rounded to a multiple of 64.
 constexpr int kAutoTargetWaves = 8192;
+// Multi-token key splits are whole numbers of this many keys (the largest
+// MFMA tile), so no tile straddles two splits.
+constexpr int kPrefillSplitQuantum = 128;
 constexpr int kMinAutoSplit = 64;
 constexpr int kMaxAutoSplit = 1024;
 
@@ -41,6 +44,7 @@ struct PlanParams {
   int group;          // query heads per KV head
   int vector_all;     // 1: every row goes to the row kernel
   int tile_rows;      // rows per MFMA multi-token work item
+  int prefill_split;  // keys per split of a multi-token sequence (0: none)
   int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
 };
 
@@ -65,6 +69,7 @@ struct AttnArgs {
   int total_q;
   float scale_log2;   // scale * log2(e)
   void* ws;
+  int prefill_split;  // keys per split of a multi-token sequence (0: none)
 };
 
 hipError_t launch_row_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,

@@ -13,13 +13,21 @@ namespace pa {
 namespace {
 
 constexpr int kPlanThreads = 256;
+constexpr int kSplitList = 256;   // split multi-token sequences whose combine items are written by all threads
+
+struct SplitSeq {
+  int32_t seq, comb_base, pbase, i0, n, L, q0, ns;
+};
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens,
                                                            const int32_t* __restrict__ qsl,
                                                            PlanParams pp, uint8_t* ws,
                                                            WorkspaceLayout lay) {
   __shared__ int32_t scan[4][kPlanThreads];
+  __shared__ SplitSeq split_list[kSplitList];
+  __shared__ int32_t split_count;
   const int tid = threadIdx.x;
+  if (tid == 0) split_count = 0;
   const int S = pp.num_seqs;
   const int per = (S + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(S, tid * per);
@@ -38,7 +46,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         c[3] += ns;
       }
     }
-    c[1] += w.tiles;
+    const TileWork tw = tile_work(n, L, pp.group, pp.tile_rows, w.tiles, pp.prefill_split);
+    c[1] += tw.items;
+    c[2] += tw.combs;
+    c[3] += tw.slots;
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) scan[k][tid] = c[k];
@@ -77,10 +88,45 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         base[0] += 1;
       }
     }
+    if (w.tiles == 0) continue;
+    // A split multi-token sequence: partial slots token-major, a combine
+    // item for every token that sees more than one split.
+    const TileWork tw = tile_work(n, L, pp.group, pp.tile_rows, w.tiles, pp.prefill_split);
+    const int ns = key_splits(L, pp.prefill_split);
+    int32_t pbase = -1;
+    if (ns > 1) {
+      pbase = base[3];
+      // The combine items of the sequence's tokens: listed for all threads
+      // to write below, or written here if the list is full.
+      const int i0 = n - tw.combs;
+      const int at = atomicAdd(&split_count, 1);
+      if (at < kSplitList) {
+        split_list[at] = SplitSeq{s, base[2], pbase, i0, n, L, qsl[s], ns};
+      } else {
+        for (int i = i0; i < n; ++i)
+          if (base[2] + i - i0 < pp.cap_combs)
+            combs[base[2] + i - i0] = CombItem{qsl[s] + i, pbase + i * ns, key_splits(L - n + i + 1, pp.prefill_split), s};
+      }
+      base[2] += tw.combs;
+      base[3] += tw.slots;
+    }
     // Last tile first: later rows see the longest causal key range.
     for (int t = w.tiles - 1; t >= 0; --t) {
-      if (base[1] < pp.cap_tiles) tiles[base[1]] = TileItem{s, t};
-      base[1] += 1;
+      const int nk = ns > 1 ? key_splits(tile_key_end(n, L, pp.group, pp.tile_rows, t), pp.prefill_split) : 1;
+      for (int k = 0; k < nk; ++k) {
+        if (base[1] < pp.cap_tiles) tiles[base[1]] = TileItem{s, t, k, pbase};
+        base[1] += 1;
+      }
+    }
+  }
+  __syncthreads();
+  const int nl = min(split_count, kSplitList);
+  for (int e = 0; e < nl; ++e) {
+    const SplitSeq q = split_list[e];
+    for (int i = q.i0 + tid; i < q.n; i += kPlanThreads) {
+      const int64_t at = (int64_t)q.comb_base + i - q.i0;
+      if (at < pp.cap_combs)
+        combs[at] = CombItem{q.q0 + i, q.pbase + i * q.ns, key_splits(q.L - q.n + i + 1, pp.prefill_split), q.seq};
     }
   }
   if (tid == kPlanThreads - 1) {

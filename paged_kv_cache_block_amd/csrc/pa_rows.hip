@@ -207,9 +207,10 @@ __global__ __launch_bounds__(64) void row_attn_kernel(AttnArgs a, PoolArgs p, Wo
   }
 }
 
-// Merge the split states of one row: thread (h, d) owns one output element.
-// Split states are fetched eight at a time with independent loads, so a row
-// with many splits costs a few memory latencies rather than one per split.
+// Merge the split states of one row: a thread owns four consecutive output
+// elements of one head.  Split states are fetched eight at a time with
+// independent loads and merged in one pass with a running max, so a row costs
+// one memory latency per eight splits.
 template <int DT>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, WorkspaceLayout lay, int D) {
   constexpr int U = 8;
@@ -218,45 +219,51 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, WorkspaceLayou
   if ((int)blockIdx.x >= pc->combs) return;
   const CombItem ci = reinterpret_cast<const CombItem*>(ws + lay.combs)[blockIdx.x];
   const int Hq = a.num_q_heads;
+  const int q4 = D >> 2;                       // 4-element groups per head
   const int e = blockIdx.y * 256 + threadIdx.x;
-  const int h = e / D;
-  const int d = e % D;
+  const int h = e / q4;
+  const int d = (e - h * q4) * 4;
   if (h >= Hq || ci.row >= a.total_q || ci.pslot < 0 || ci.pslot + ci.nsplit > lay.cap_partials) return;
-  const float* po = reinterpret_cast<const float*>(ws + lay.part_o) + (int64_t)ci.pslot * Hq * D + h * D + d;
+  const float4* po = reinterpret_cast<const float4*>(
+      reinterpret_cast<const float*>(ws + lay.part_o) + (int64_t)ci.pslot * Hq * D + h * D + d);
   const float2* pm = reinterpret_cast<const float2*>(ws + lay.part_ml) + (int64_t)ci.pslot * Hq + h;
-  const int64_t so = (int64_t)Hq * D;   // stride between splits, in floats
-  float mx = -INFINITY;
+  const int64_t so = (int64_t)Hq * D / 4;      // stride between splits, in float4
+  float m = -INFINITY, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int k0 = 0; k0 < ci.nsplit; k0 += U) {
     float2 ml[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) ml[u] = k0 + u < ci.nsplit ? pm[(int64_t)(k0 + u) * Hq] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (ml[u].y > 0.f) mx = fmaxf(mx, ml[u].x);
-  }
-  float lsum = 0.f, o = 0.f;
-  for (int k0 = 0; k0 < ci.nsplit; k0 += U) {
-    float2 ml[U];
-    float acc[U];
+    float4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = k0 + u < ci.nsplit;
       ml[u] = in ? pm[(int64_t)(k0 + u) * Hq] : make_float2(-INFINITY, 0.f);
-      acc[u] = in ? po[(int64_t)(k0 + u) * so] : 0.f;
+      o[u] = in ? po[(int64_t)(k0 + u) * so] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (!(ml[u].y > 0.f)) continue;
-      const float w = fast_exp2(ml[u].x - mx);
-      lsum += w * ml[u].y;
-      o += w * acc[u];
+      if (!(ml[u].y > 0.f)) continue;          // a split with no visible key
+      const float mn = fmaxf(m, ml[u].x);
+      const float sa = fast_exp2(m - mn);      // 0 while nothing is merged yet
+      const float sb = fast_exp2(ml[u].x - mn);
+      l = l * sa + ml[u].y * sb;
+      acc.x = acc.x * sa + o[u].x * sb;
+      acc.y = acc.y * sa + o[u].y * sb;
+      acc.z = acc.z * sa + o[u].z * sb;
+      acc.w = acc.w * sa + o[u].w * sb;
+      m = mn;
     }
   }
-  const float v = o / lsum;
+  const float inv = 1.f / l;
   const int64_t at = ((int64_t)ci.row * Hq + h) * D + d;
-  if constexpr (DT == DT_F32) reinterpret_cast<uint32_t*>(a.out)[at] = __float_as_uint(v);
-  else if constexpr (DT == DT_F16) reinterpret_cast<uint16_t*>(a.out)[at] = f32_to_f16_bits(v);
-  else reinterpret_cast<uint16_t*>(a.out)[at] = f32_to_bf16_bits(v);
+  if constexpr (DT == DT_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + at) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  } else {
+    uint2 w;
+    w.x = pack2<DT>(acc.x * inv, acc.y * inv);
+    w.y = pack2<DT>(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + at) = w;
+  }
 }
 
 template <int DT, int D, int BS, int GH>
@@ -317,7 +324,7 @@ hipError_t launch_row_attention(const AttnArgs& a, const PoolArgs& p, const Work
 hipError_t launch_combine(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                           int num_combs, hipStream_t s) {
   if (num_combs == 0) return hipSuccess;
-  const dim3 grid(num_combs, (a.num_q_heads * p.head_dim + 255) / 256);
+  const dim3 grid(num_combs, (a.num_q_heads * p.head_dim / 4 + 255) / 256);
   switch (p.dtype) {
     case DT_F32: hipLaunchKernelGGL(combine_kernel<DT_F32>, grid, dim3(256), 0, s, a, lay, p.head_dim); break;
     case DT_F16: hipLaunchKernelGGL(combine_kernel<DT_F16>, grid, dim3(256), 0, s, a, lay, p.head_dim); break;

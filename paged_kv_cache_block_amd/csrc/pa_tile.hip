@@ -159,6 +159,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   // Key ranges: the workgroup's and this wave's (rows ascend, so the last
   // row of a range has the largest causal limit, the first the smallest).
   const int kend = L - n + (min(R, r0 + TROWS) - 1) / G + 1;
+  // Keys of this item: the whole causal range, or one split of it.
+  const int S = a.prefill_split;
+  const int k0 = ti.pslot < 0 ? 0 : ti.split * S;
+  const int k1 = ti.pslot < 0 ? kend : min(kend, k0 + S);
   const bool wave_on = wr0 < R;
   const bool wave_full = wr0 + 32 <= R;
   const int wfirst = wave_on ? L - n + wr0 / G : 0;
@@ -260,7 +264,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
     for (int j = 0; j < VCH; ++j) *reinterpret_cast<u32x4*>(vd_ + VRP * j * VROW) = b.v[j];
   };
 
-  const int ntiles = (kend + kKeys - 1) / kKeys;
+  const int kt_first = k0 / kKeys;                 // splits are whole tiles
+  const int kt_end = (k1 + kKeys - 1) / kKeys;
   const int krow = row_key(col);
   const int wend = wave_on ? L - n + (min(R, wr0 + 32) - 1) / G + 1 : 0;
   // LDS operand reads of one 32-key half: K rows for S^T, V^T rows for O^T.
@@ -353,21 +358,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   // iterations to arrive; a 128-key iteration is long enough on its own.
   // Past the last tile, loads and stores repeat the last tile into an idle
   // stage.
-  const int last = ntiles - 1;
+  const int last = kt_end - 1;
   if constexpr (NW == 8) {
     Buf ba;
-    load_tile(ba, 0);
-    zero_tail(ba, 0);
+    load_tile(ba, kt_first);
+    zero_tail(ba, kt_first);
     store_tile(ba, 0);
-    load_tile(ba, min(1, last));
+    load_tile(ba, min(kt_first + 1, last));
     __syncthreads();
-    for (int kt = 0; kt < ntiles; kt += 2) {
+    for (int kt = kt_first; kt < kt_end; kt += 2) {
       compute(kt, 0);
       zero_tail(ba, min(kt + 1, last));
       store_tile(ba, 1);
       load_tile(ba, min(kt + 2, last));
       __syncthreads();
-      if (kt + 1 >= ntiles) break;
+      if (kt + 1 >= kt_end) break;
       compute(kt + 1, 1);
       zero_tail(ba, min(kt + 2, last));
       store_tile(ba, 0);
@@ -376,19 +381,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
     }
   } else {
     Buf ba, bb;
-    load_tile(ba, 0);
-    zero_tail(ba, 0);
+    load_tile(ba, kt_first);
+    zero_tail(ba, kt_first);
     store_tile(ba, 0);
-    load_tile(ba, min(1, last));
-    load_tile(bb, min(2, last));
+    load_tile(ba, min(kt_first + 1, last));
+    load_tile(bb, min(kt_first + 2, last));
     __syncthreads();
-    for (int kt = 0; kt < ntiles; kt += 2) {
+    for (int kt = kt_first; kt < kt_end; kt += 2) {
       compute(kt, 0);
       zero_tail(ba, min(kt + 1, last));
       store_tile(ba, 1);
       load_tile(ba, min(kt + 3, last));
       __syncthreads();
-      if (kt + 1 >= ntiles) break;
+      if (kt + 1 >= kt_end) break;
       compute(kt + 1, 1);
       zero_tail(bb, min(kt + 2, last));
       store_tile(bb, 0);
@@ -398,18 +403,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   }
 
   if (!row_ok) return;
-  const float inv = 1.f / l_run;
-  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q0 + qi) * Hq + hq) * D;
+  const int ns_row = ti.pslot < 0 ? 1 : key_splits(p_row + 1, S);
+  if (ns_row == 1) {
+    // All of this row's keys are in split 0: normalise and store.
+    if (ti.split != 0) return;
+    const float inv = 1.f / l_run;
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q0 + qi) * Hq + hq) * D;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
+    for (int t = 0; t < NDT; ++t) {
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int d = 32 * t + 8 * a4 + 4 * hh;
-      uint2 w;
-      w.x = cvt2<DT>(o[t][4 * a4] * inv, o[t][4 * a4 + 1] * inv);
-      w.y = cvt2<DT>(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d) = w;
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * t + 8 * a4 + 4 * hh;
+        uint2 w;
+        w.x = cvt2<DT>(o[t][4 * a4] * inv, o[t][4 * a4 + 1] * inv);
+        w.y = cvt2<DT>(o[t][4 * a4 + 2] * inv, o[t][4 * a4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + d) = w;
+      }
     }
+    return;
+  }
+  // The row's partial state over this split (none if no key of the row is
+  // in it); the combine kernel merges the splits.
+  if (p_row < k0) return;
+  const int64_t slot = (int64_t)ti.pslot + (int64_t)qi * key_splits(L, S) + ti.split;
+  if (slot >= lay.cap_partials) return;
+  float* po = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + lay.part_o) + (slot * Hq + hq) * D;
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4)
+      *reinterpret_cast<float4*>(po + 32 * t + 8 * a4 + 4 * hh) =
+          make_float4(o[t][4 * a4], o[t][4 * a4 + 1], o[t][4 * a4 + 2], o[t][4 * a4 + 3]);
+  if (hh == 0) {
+    float2* pm = reinterpret_cast<float2*>(const_cast<uint8_t*>(ws) + lay.part_ml);
+    pm[slot * Hq + hq] = make_float2(m_run, l_run);
   }
 }
 

@@ -82,7 +82,8 @@ def test_write_and_copy_bit_exact(torch_cuda, cfg):
     assert np.array_equal(bits(gv), bits(v)), "V pool differs"
 
 
-@pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream", "tile128", "tile256"])
+@pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream", "tile128", "tile256",
+                                  "psplit128", "psplit128w"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_attention_small(torch_cuda, cfg, mode):
     from paged_kv_cache_block_amd import binding
@@ -90,7 +91,9 @@ def test_attention_small(torch_cuda, cfg, mode):
            "rows": binding.options(0, 0, binding.PA_FLAG_VECTOR_ALU),
            "stream": binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED),
            "tile128": binding.options(prefill_tile_rows=128),
-           "tile256": binding.options(prefill_tile_rows=256)}[mode]
+           "tile256": binding.options(prefill_tile_rows=256),
+           "psplit128": binding.options(prefill_split_tokens=128),
+           "psplit128w": binding.options(prefill_split_tokens=128, prefill_tile_rows=256)}[mode]
     w = small_workload(cfg)
     say("attention", w.name, mode)
     db = run_gpu(w, opt)
@@ -180,6 +183,41 @@ def test_split_lengths_agree(torch_cuda):
         compare(db.out_numpy(), want, w.dtype, what=f"split {split}")
 
 
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_prefill_split_lengths_agree(torch_cuda, cfg):
+    """Multi-token contexts split into 128..4096-key ranges, merged by the
+    combine kernel (tokens with one, two and three splits), on both tile
+    sizes and together with split decode rows."""
+    from paged_kv_cache_block_amd import binding
+    w = small_workload(cfg)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    for psplit in (100, 128, 256, 384, 4096):
+        for rows in (128, 256):
+            for dsplit in (0, 64):
+                say("prefill split", psplit, "tile rows", rows, "decode split", dsplit)
+                db = run_gpu(w, binding.options(dsplit, psplit, prefill_tile_rows=rows))
+                compare(db.out_numpy(), want, w.dtype,
+                        what=f"{w.name} prefill split {psplit} rows {rows} decode split {dsplit}")
+
+
+@pytest.mark.parametrize("psplit", [0, 128, 1024])
+def test_chunk_recompute_shape(torch_cuda, psplit):
+    """32-token chunks after 0..3000 cached tokens (the chunk recomputation
+    the cost profile measures), whole and with split contexts."""
+    from paged_kv_cache_block_amd import binding
+    seqs = [(0, 32, 1), (31, 32, 1), (700, 32, 2), (3000, 32, 1)]
+    w = build_batch("32-token chunks bf16", "bf16", 64, 8, 128, 32, 256, seqs, 77)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    for rows in (128, 256):
+        say("chunk shape split", psplit, "rows", rows)
+        db = run_gpu(w, binding.options(0, psplit, prefill_tile_rows=rows))
+        compare(db.out_numpy(), want, w.dtype, what=f"chunks split {psplit} rows {rows}")
+
+
 def test_edge_cases(torch_cuda):
     """Sequences with no new tokens, one-token contexts, prefills without
     history, sub-requests sharing one block-table row, and a ragged tail."""
@@ -251,11 +289,12 @@ def _sample(w, k):
     return sorted(int(s) for s in pick)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_full_config_sampled(torch_cuda, cfg):
+@pytest.mark.parametrize("cfg,psplit", [(1, 0), (2, 0), (3, 0), (4, 0), (5, 0), (3, 512), (5, 1024)])
+def test_full_config_sampled(torch_cuda, cfg, psplit):
+    from paged_kv_cache_block_amd import binding
     w = config_workload(cfg)
-    say("full", w.name)
-    db = run_gpu(w)
+    say("full", w.name, "prefill split", psplit)
+    db = run_gpu(w, binding.options(prefill_split_tokens=psplit) if psplit else None)
     got = db.out_numpy()
     assert np.isfinite(oracle.to_f64(got, w.dtype)).all(), "non-finite output"
     k, v = oracle_step(w)
