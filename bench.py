@@ -234,6 +234,168 @@ def chunk_cost(args) -> int:
     return 0
 
 
+def _time_ms(fn, reps: int) -> float:
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _contiguous(w):
+    """The same batch with every sequence's blocks renumbered to consecutive
+    physical ids in table order (identity-like placement)."""
+    import copy
+    bs = w.block_size
+    perm = np.full(w.num_blocks, -1, np.int64)
+    nxt = 0
+    for si, L in enumerate(w.context_lens):
+        for b in w.block_tables[si, :-(-int(L) // bs)]:
+            if perm[b] < 0:
+                perm[b] = nxt
+                nxt += 1
+    rest = np.flatnonzero(perm < 0)
+    perm[rest] = np.arange(nxt, nxt + rest.size)
+
+    def slots(sl):
+        sl = np.asarray(sl, dtype=np.int64)
+        return np.where(sl >= 0, perm[sl // bs] * bs + sl % bs, sl)
+    w2 = copy.copy(w)
+    w2.hist_slots = slots(w.hist_slots)
+    w2.slot_mapping = slots(w.slot_mapping)
+    w2.block_tables = perm[w.block_tables].astype(np.int32)
+    w2.cow_pairs = perm[np.asarray(w.cow_pairs, dtype=np.int64)].astype(np.int32).reshape(-1, 2)
+    return w2
+
+
+def paging(args) -> int:
+    """Paging-overhead and batching diagnostics on the two headline shapes.
+
+    The vLLM wiki page (实验与结果: the paged kernel is 20-26% slower than a
+    contiguous one; block sizes 16-128 work well) and the Pensieve page
+    (figures 12-13: copying K/V out before attending costs a lot; one
+    unified call for prefill and decode) measure these effects.  For the
+    decode shape (64 fp16 decodes, 40 heads x 128) and the multi-token shape
+    (16 x 512-token prefills over 3000-4096 cached tokens, 64/8 heads x 128,
+    bf16) this prints, one JSON line each:
+    - block size 16, 32, 64, 128: attention time, and the slots allocated
+      but unused in each sequence's last block;
+    - contiguous (identity) block placement vs a shuffled pool;
+    - copy-out: gathering every context into contiguous blocks with
+      pa_copy_blocks and then attending, vs attending in place;
+    - for the two mixed batches, one unified call vs separate prefill and
+      decode calls.
+    """
+    import torch
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.step import DeviceBatch
+    from workloads import build_batch, config_workload
+
+    reps = max(args.steps, 5)
+    rng = np.random.default_rng(11)
+    dec_lens = rng.integers(128, 2049, size=64)
+    shapes = {
+        "decode": ("f16", 40, 40, 128, [(int(L) - 1, 1, 1) for L in dec_lens]),
+        "multi_token": ("bf16", 64, 8, 128,
+                        [(int(h), 512, 1) for h in rng.integers(3000, 4097, size=16)]),
+    }
+
+    def emit(d):
+        print(json.dumps({"paging": d}), flush=True)
+
+    def attend_ms(db, tables=None):
+        bt = db.block_tables if tables is None else tables
+        return _time_ms(lambda: binding.pa_attention(
+            db.out, db.q, db.k_cache, db.v_cache, bt, db.context_lens, db.query_start_loc,
+            db.context_lens_host, db.qsl_host, db.w.scale, db.workspace, db.opt), reps)
+
+    for name, (dt, hq, hkv, d, seqs) in shapes.items():
+        tokens = sum(h + n for h, n, _ in seqs)
+        for bs in (16, 32, 64, 128):
+            need = sum(-(-(h + n) // bs) for h, n, _ in seqs)
+            nb = 2 * need + 16                        # room for a contiguous copy
+            shuffled = build_batch(f"{name} bs {bs}", dt, hq, hkv, d, bs, nb, seqs, 5)
+            for placement in ("shuffled", "contiguous"):
+                w = shuffled if placement == "shuffled" else _contiguous(shuffled)
+                db = DeviceBatch(w, opt=binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED))
+                db.write_history()
+                db.write_new()
+                torch.cuda.synchronize()
+                ms = attend_ms(db)
+                rec = {"shape": name, "block_size": bs, "placement": placement,
+                       "attention_ms": round(ms, 4),
+                       "unused_slots_frac": round(1 - tokens / (need * bs), 4)}
+                if placement == "shuffled":
+                    # Copy-out: gather every context into blocks no sequence
+                    # uses (in table order), then attend there.
+                    tbl = w.block_tables
+                    live = np.zeros(nb, bool)
+                    for si, L in enumerate(w.context_lens):
+                        live[tbl[si, :-(-int(L) // bs)]] = True
+                    free = iter(np.flatnonzero(~live).tolist())
+                    pairs, ctab = [], np.zeros_like(tbl)
+                    for si, L in enumerate(w.context_lens):
+                        for j in range(-(-int(L) // bs)):
+                            dst = next(free)
+                            pairs.append((int(tbl[si, j]), dst))
+                            ctab[si, j] = dst
+                    pairs_t = torch.tensor(pairs, dtype=torch.int32, device="cuda")
+                    ctab_t = torch.from_numpy(ctab).to("cuda")
+
+                    def copy_then_attend():
+                        binding.pa_copy_blocks(db.k_cache, db.v_cache, pairs_t)
+                        binding.pa_attention(db.out, db.q, db.k_cache, db.v_cache, ctab_t,
+                                             db.context_lens, db.query_start_loc,
+                                             db.context_lens_host, db.qsl_host, w.scale,
+                                             db.workspace, db.opt)
+                    rec["copy_out_then_attend_ms"] = round(_time_ms(copy_then_attend, reps), 4)
+                emit(rec)
+                del db
+                torch.cuda.empty_cache()
+
+    for cfg in (3, 5):
+        w = config_workload(cfg)
+        db = DeviceBatch(w)
+        db.write_history()
+        db.write_new()
+        torch.cuda.synchronize()
+        unified = attend_ms(db)
+        n = np.diff(w.query_start_loc)
+        parts = []
+        for sel in (n > 1, n == 1):
+            idx = np.flatnonzero(sel)
+            qsl = np.zeros(idx.size + 1, np.int32)
+            qsl[1:] = np.cumsum(n[idx])
+            rows = np.concatenate([np.arange(w.query_start_loc[i], w.query_start_loc[i + 1]) for i in idx])
+            sub = dict(bt=torch.from_numpy(np.ascontiguousarray(w.block_tables[idx])).to("cuda"),
+                       lens=torch.from_numpy(np.ascontiguousarray(w.context_lens[idx])).to("cuda"),
+                       qsl=torch.from_numpy(qsl).to("cuda"),
+                       lens_h=torch.from_numpy(np.ascontiguousarray(w.context_lens[idx])),
+                       qsl_h=torch.from_numpy(qsl.copy()),
+                       q=db.q[torch.from_numpy(rows).to("cuda")].contiguous())
+            sub["out"] = torch.empty_like(sub["q"])
+            sub["ws"] = torch.empty(binding.pa_attention_workspace_size(
+                db.desc, w.num_q_heads, idx.size, int(qsl[-1]), int(w.context_lens[idx].max())),
+                dtype=torch.uint8, device="cuda")
+            parts.append(sub)
+
+        def separate():
+            for sb in parts:
+                binding.pa_attention(sb["out"], sb["q"], db.k_cache, db.v_cache, sb["bt"], sb["lens"],
+                                     sb["qsl"], sb["lens_h"], sb["qsl_h"], w.scale, sb["ws"])
+        emit({"batch": w.name, "unified_call_ms": round(unified, 4),
+              "separate_calls_ms": round(_time_ms(separate, reps), 4)})
+        del db, parts
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +414,8 @@ def main(argv=None) -> int:
                     help="only run pa_copy_blocks over a known byte count (scales HBM counters)")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only measure reference HBM rates (torch sum and copy, pa_copy_blocks)")
+    ap.add_argument("--paging", action="store_true",
+                    help="paging diagnostics: block sizes, contiguous vs shuffled, copy-out, unified vs split calls")
     ap.add_argument("--chunk-cost", action="store_true",
                     help="time one 32-token chunk (and 16 of them) after 0..32K cached tokens, then exit")
     ap.add_argument("--mfma-reference", action="store_true",
@@ -279,6 +443,8 @@ def main(argv=None) -> int:
         return mfma_reference()
     if args.chunk_cost:
         return chunk_cost(args)
+    if args.paging:
+        return paging(args)
     t0 = time.time()
     w = config_workload(args.config, args.seed)
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)

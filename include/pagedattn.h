@@ -39,11 +39,12 @@
  *  i.e. inside a block and head, K is token-major and V is head-dim-major.
  *  A slot is block * block_size + offset.
  *
- *  Supported shapes: head_dim 64 or 128; block_size 4, 8, 16 or 32 for every
- *  dtype (the MFMA multi-token path needs block_size 16 or 32 and a 16-bit
- *  dtype; other cases take a vector-ALU path with the same results within
- *  tolerance); num_q_heads a multiple of num_kv_heads with a group of 1, 2,
- *  4, 8 or 16 query heads per KV head.
+ *  Supported shapes: head_dim 64 or 128; block_size 4, 8, 16, 32 or 64 for
+ *  every dtype, and 128 for fp16 / bf16 (the MFMA decode and multi-token
+ *  paths take block_size 16..128 and a 16-bit dtype; other cases take a
+ *  vector-ALU path with the same results within tolerance, which has no
+ *  128-token blocks); num_q_heads a multiple of num_kv_heads with a group of
+ *  1, 2, 4, 8 or 16 query heads per KV head.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H

@@ -46,8 +46,9 @@ pa_status check_desc(const pa_cache_desc* c, PoolArgs* p) {
     return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", c->dtype);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", c->head_dim);
-  if (c->block_size != 4 && c->block_size != 8 && c->block_size != 16 && c->block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (4, 8, 16, 32)", c->block_size);
+  if (c->block_size != 4 && c->block_size != 8 && c->block_size != 16 && c->block_size != 32 &&
+      c->block_size != 64 && c->block_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (4, 8, 16, 32, 64, 128)", c->block_size);
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_blocks and num_kv_heads must be positive");
   *p = PoolArgs{c->num_blocks, c->block_size, c->num_kv_heads, c->head_dim, c->dtype};
@@ -328,6 +329,9 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
     return fail(PA_ERR_WORKSPACE, "plan exceeds workspace capacity");
   if (n_rows > 0x7fffffff || n_tiles > 0x7fffffff)
     return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
+  const bool rows_on_mfma = !va && decode_mfma_supported(p, group);
+  if (n_rows > 0 && !rows_on_mfma && p.block_size > 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d needs the fp16/bf16 MFMA kernels", p.block_size);
 
   PlanParams pp{num_seqs, split, group, va ? 1 : 0, tile_rows, psplit,
                 lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials};
@@ -349,7 +353,7 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   }
   if (n_rows > 0) {
     mark(PA_TIME_ROWS, opt ? opt->timing_start : nullptr);
-    e = (!va && decode_mfma_supported(p, group))
+    e = rows_on_mfma
             ? launch_decode_mfma(a, p, lay, (int)n_rows, split,
                                  opt && (opt->flags & PA_FLAG_KV_UNSHARED), stream)
             : launch_row_attention(a, p, lay, (int)n_rows, split, stream);

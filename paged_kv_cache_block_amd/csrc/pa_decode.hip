@@ -57,7 +57,9 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 16-byte load; NT streams past the caches (data read once).
+// 16-byte load; NT streams past the caches (data read once).  A 32-key step
+// reads only part of each V^T row of a block larger than 32 tokens, and the
+// next step reads the rest, so those loads keep the caches.
 template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
   if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
                                                          WorkspaceLayout lay, int split_tokens) {
   constexpr int KS = D / 32;
   constexpr int NDT = D / 16;
-  static_assert(BS == 16 || BS == 32, "block size");
+  static_assert(BS == 16 || BS % 32 == 0, "a 32-key step spans two blocks of 16 or lies in one block");
 
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
   const PlanCounts* pc = reinterpret_cast<const PlanCounts*>(ws + lay.counts);
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
       const uint16_t* vp = vc + (((int64_t)blk * Hkv + g) * D + c16) * BS + off;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        st.v[dt] = ld16<NT>(vp + (int64_t)16 * dt * BS);
+        st.v[dt] = ld16<NT && BS <= 32>(vp + (int64_t)16 * dt * BS);
     }
   };
 
@@ -257,6 +259,10 @@ hipError_t launch_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout&
     hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 16, NT>), grid, dim3(64), 0, s, a, p, lay, split);
   else if (p.block_size == 32)
     hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 32, NT>), grid, dim3(64), 0, s, a, p, lay, split);
+  else if (p.block_size == 64)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 64, NT>), grid, dim3(64), 0, s, a, p, lay, split);
+  else if (p.block_size == 128)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 128, NT>), grid, dim3(64), 0, s, a, p, lay, split);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -272,7 +278,7 @@ hipError_t launch_nt(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout
 }  // namespace
 
 bool decode_mfma_supported(const PoolArgs& p, int group) {
-  return (p.dtype == DT_F16 || p.dtype == DT_BF16) && (p.block_size == 16 || p.block_size == 32) &&
+  return (p.dtype == DT_F16 || p.dtype == DT_BF16) && (p.block_size == 16 || p.block_size == 32 || p.block_size == 64 || p.block_size == 128) &&
          (p.head_dim == 64 || p.head_dim == 128) && group <= 16;
 }
 

@@ -296,6 +296,7 @@ hipError_t launch_rows_bs(const AttnArgs& a, const PoolArgs& p, const WorkspaceL
     case 8: return launch_rows_g<DT, D, 8>(a, p, lay, num_items, split_tokens, s);
     case 16: return launch_rows_g<DT, D, 16>(a, p, lay, num_items, split_tokens, s);
     case 32: return launch_rows_g<DT, D, 32>(a, p, lay, num_items, split_tokens, s);
+    case 64: return launch_rows_g<DT, D, 64>(a, p, lay, num_items, split_tokens, s);
   }
   return hipErrorInvalidValue;
 }

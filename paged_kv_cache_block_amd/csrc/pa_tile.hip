@@ -227,15 +227,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
     ensure_window(kt);
     const int kt0 = kt * kKeys;
     const int b0 = kt0 / BS - win * kTabWin;
+    const int kin = kt0 % BS;          // tile start inside its block (blocks larger than a tile)
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
       const unsigned blk = btab[b0 + (ktok + KRP * j) / BS];
-      b.k[j] = *reinterpret_cast<const u32x4*>(kc + blk * kstride + kofs[j]);
+      b.k[j] = *reinterpret_cast<const u32x4*>(kc + blk * kstride + kofs[j] + kin * D);
     }
     const unsigned vblk = btab[b0 + vkey / BS];
 #pragma unroll
     for (int j = 0; j < VCH; ++j)
-      b.v[j] = *reinterpret_cast<const u32x4*>(vc + vblk * kstride + vofs[j]);
+      b.v[j] = *reinterpret_cast<const u32x4*>(vc + vblk * kstride + vofs[j] + kin);
   };
   // Tail tile: slots at or past kend may be unwritten (NaN).  Zero the V
   // entries (a zero probability must not meet them); K rows there are masked
@@ -448,6 +449,10 @@ hipError_t launch_tile_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLa
     hipLaunchKernelGGL((tile_attn_kernel<DT, D, 16, NW>), grid, dim3(64 * NW), 0, s, a, p, lay, num_tiles);
   else if (p.block_size == 32)
     hipLaunchKernelGGL((tile_attn_kernel<DT, D, 32, NW>), grid, dim3(64 * NW), 0, s, a, p, lay, num_tiles);
+  else if (p.block_size == 64)
+    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 64, NW>), grid, dim3(64 * NW), 0, s, a, p, lay, num_tiles);
+  else if (p.block_size == 128)
+    hipLaunchKernelGGL((tile_attn_kernel<DT, D, 128, NW>), grid, dim3(64 * NW), 0, s, a, p, lay, num_tiles);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -464,7 +469,7 @@ hipError_t launch_tile_cb(const AttnArgs& a, const PoolArgs& p, const WorkspaceL
 }  // namespace
 
 bool tile_path_supported(const PoolArgs& p) {
-  return (p.dtype == DT_F16 || p.dtype == DT_BF16) && (p.block_size == 16 || p.block_size == 32) &&
+  return (p.dtype == DT_F16 || p.dtype == DT_BF16) && (p.block_size == 16 || p.block_size == 32 || p.block_size == 64 || p.block_size == 128) &&
          (p.head_dim == 64 || p.head_dim == 128);
 }
 

@@ -47,6 +47,9 @@ def test_workspace_size_is_host_only(binding):
     # forcing short splits needs more room for partial states
     small = binding.pa_attention_workspace_size(d, 40, 64, 64, 2048, binding.options(64))
     assert small > n
+    # so does splitting multi-token contexts
+    psplit = binding.pa_attention_workspace_size(d, 40, 64, 64, 2048, binding.options(0, 512))
+    assert psplit > n
     assert binding.pa_attention_workspace_size(d, 41, 64, 64, 2048) == 0   # 41 % 40 != 0
 
 
@@ -63,7 +66,7 @@ def _call_attention(b, desc, hq, lens, qsl, ws_bytes=1 << 20, opt=None):
 @pytest.mark.parametrize("case,expect", [
     ("bad_dtype", -2), ("bad_head_dim", -2), ("bad_block", -2), ("heads", -1),
     ("group", -2), ("n_gt_L", -1), ("qsl_order", -1), ("qsl_total", -1), ("too_long", -1),
-    ("workspace", -3), ("flags", -1)])
+    ("workspace", -3), ("flags", -1), ("neg_split", -1), ("block128_vector", -2)])
 def test_attention_argument_errors(binding, case, expect):
     b = binding
     desc = _desc(b)
@@ -91,6 +94,11 @@ def test_attention_argument_errors(binding, case, expect):
         ws = 10
     elif case == "flags":
         opt = b.options(0, 0, 4)
+    elif case == "neg_split":
+        opt = b.options(0, -128)
+    elif case == "block128_vector":   # fp32 rows take the vector-ALU kernel: no 128-token blocks
+        desc.block_size = 128
+        ws = 1 << 30
     st = _call_attention(b, desc, hq, lens, qsl, ws, opt)
     assert st == expect, (case, st, b.LIB.pa_last_error())
     assert b.LIB.pa_last_error()

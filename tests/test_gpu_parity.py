@@ -142,6 +142,7 @@ SHAPES = [  # (dtype, H_q, H_kv, D, block_size)
     ("bf16", 8, 8, 128, 16), ("bf16", 16, 8, 64, 16), ("bf16", 32, 4, 128, 32),
     ("f32", 4, 4, 128, 16), ("f32", 8, 2, 64, 32), ("f32", 16, 1, 64, 8),
     ("f16", 4, 2, 128, 8), ("bf16", 8, 1, 64, 4),
+    ("f16", 8, 4, 128, 64), ("bf16", 16, 2, 128, 128), ("bf16", 8, 8, 64, 128), ("f32", 8, 8, 64, 64),
 ]
 
 
