@@ -82,6 +82,46 @@ def test_write_and_copy_bit_exact(torch_cuda, cfg):
     assert np.array_equal(bits(gv), bits(v)), "V pool differs"
 
 
+@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 32), ("f32", 8), ("f16", 128)])
+def test_write_kv_runs_and_gaps(torch_cuda, dtype, bs):
+    """The scatter with slot runs that are aligned, misaligned, cross a block
+    boundary, skip (negative slots) and end in a ragged tail: bit-exact."""
+    torch = torch_cuda
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.step import NAN_FILL, TORCH_DTYPE, to_numpy, to_torch
+    from workloads import round_to_dtype
+    nb, h, d = 64, 3, 64
+    rng = np.random.default_rng(bs)
+    runs = [list(range(8 * bs, 8 * bs + 16)),              # two aligned 8-runs
+            list(range(5 * bs + 4, 5 * bs + 12)),          # misaligned
+            list(range(2 * bs - 4, 2 * bs + 4)),           # crosses a block boundary
+            [-1, 3 * bs + 1, -1, 3 * bs + 2, 40 * bs, 41 * bs + 3, -5, 12 * bs + 7],
+            list(range(20 * bs, 20 * bs + 5))]             # ragged tail
+    slots = np.array([x for r in runs for x in r], dtype=np.int64)
+    t = slots.size
+    kn = round_to_dtype(rng.standard_normal((t, h, d), dtype=np.float32), dtype)
+    vn = round_to_dtype(rng.standard_normal((t, h, d), dtype=np.float32), dtype)
+    dt = TORCH_DTYPE[dtype]
+    kc = torch.empty((nb, h, bs, d), dtype=dt, device="cuda")
+    vc = torch.empty((nb, h, d, bs), dtype=dt, device="cuda")
+    it, fill = NAN_FILL[dtype]
+    kc.view(it).fill_(fill)
+    vc.view(it).fill_(fill)
+    say("write runs", dtype, bs)
+    binding.pa_write_kv(to_torch(kn, dtype, "cuda"), to_torch(vn, dtype, "cuda"),
+                        torch.from_numpy(slots).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    k0 = to_numpy(kc, dtype).copy()
+    v0 = to_numpy(vc, dtype).copy()
+    # expected: the poisoned pools with the oracle's scatter applied
+    ke, ve = np.empty_like(k0), np.empty_like(v0)
+    ke.view(np.uint32 if dtype == "f32" else np.uint16)[...] = fill & (0xFFFFFFFF if dtype == "f32" else 0xFFFF)
+    ve.view(np.uint32 if dtype == "f32" else np.uint16)[...] = fill & (0xFFFFFFFF if dtype == "f32" else 0xFFFF)
+    oracle.write_kv(ke, ve, kn, vn, slots)
+    assert np.array_equal(bits(k0), bits(ke))
+    assert np.array_equal(bits(v0), bits(ve))
+
+
 @pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream", "tile128", "tile256",
                                   "psplit128", "psplit128w"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
