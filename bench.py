@@ -393,6 +393,110 @@ def paging(args) -> int:
               "separate_calls_ms": round(_time_ms(separate, reps), 4)})
         del db, parts
         torch.cuda.empty_cache()
+
+    # Copy-on-write copies of one step on a 32-layer model: one launch for all
+    # layers vs one launch per layer (the config-4 shape: 180 pairs of bf16
+    # blocks, 2 KV heads x 16 tokens x 128).
+    layers, nb, h, bs, d = 32, 4096, 2, 16, 128
+    ks = [torch.zeros((nb, h, bs, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    vs = [torch.zeros((nb, h, d, bs), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    perm = np.random.default_rng(4).permutation(nb)
+    pairs = torch.from_numpy(np.stack([perm[:180], perm[180:360]], 1).astype(np.int32)).cuda()
+    moved = 2 * 2 * 180 * h * bs * d * 2 * layers            # read + write, K + V
+    one = _time_ms(lambda: binding.pa_copy_blocks_layers(ks, vs, pairs), reps)
+    per = _time_ms(lambda: [binding.pa_copy_blocks(k, v, pairs) for k, v in zip(ks, vs)], reps)
+    emit({"copy_on_write_layers": layers, "pairs": 180, "bytes_moved": moved,
+          "one_launch_ms": round(one, 4), "one_launch_GBs": round(moved / one / 1e6, 1),
+          "launch_per_layer_ms": round(per, 4), "launch_per_layer_GBs": round(moved / per / 1e6, 1)})
+    return 0
+
+
+def swap(args) -> int:
+    """Host <-> device block swaps on the DMA engines (pa_swap_blocks).
+
+    - rates for one run of consecutive blocks and for scattered blocks, both
+      directions (bf16, 8 KV heads x 128, block 32: 128 KB of K+V a block);
+    - swap-in and swap-out at the same time on two streams vs one after the
+      other (the Pensieve page, 实现细节与优化, saw both directions slow down
+      by 18-20% when concurrent);
+    - a 16-layer step: every layer swaps 64 blocks in and runs the 64-decode
+      attention batch; all swaps first, then all attention, vs the layer-wise
+      pipeline that gates each layer's attention on its own event.
+    """
+    import torch
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.step import DeviceBatch
+    from paged_kv_cache_block_amd.swap import LayerSwap, LayerSwapPipeline
+    from workloads import config_workload
+
+    reps = max(args.steps, 5)
+
+    def emit(d):
+        print(json.dumps({"swap": d}), flush=True)
+
+    nb, h, bs, d = 4096, 8, 32, 128
+    blk = 2 * h * bs * d * 2
+    dk = torch.zeros((nb, h, bs, d), dtype=torch.bfloat16, device="cuda")
+    dv = torch.zeros((nb, h, d, bs), dtype=torch.bfloat16, device="cuda")
+    hk = torch.zeros((nb, h, bs, d), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros((nb, h, d, bs), dtype=torch.bfloat16).pin_memory()
+    n = 1024
+    rng = np.random.default_rng(1)
+    run = np.stack([np.arange(n), np.arange(n) + 2048], 1).astype(np.int32)
+    scat = np.stack([rng.permutation(nb)[:n], rng.permutation(nb)[:n]], 1).astype(np.int32)
+    for name, pairs in (("run", run), ("scattered", scat)):
+        pt = torch.from_numpy(pairs)
+        for dname, dirn in (("in", binding.PA_SWAP_IN), ("out", binding.PA_SWAP_OUT)):
+            ms = _time_ms(lambda: binding.pa_swap_blocks(dk, dv, hk, hv, pt, dirn), reps)
+            emit({"pairs": name, "direction": dname, "blocks": n, "bytes": n * blk,
+                  "ms": round(ms, 4), "GBs": round(n * blk / ms / 1e6, 1)})
+    pin, pout = torch.from_numpy(run), torch.from_numpy(run[:, ::-1].copy())
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def concurrent():
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        binding.pa_swap_blocks(dk, dv, hk, hv, pin, binding.PA_SWAP_IN, stream=s1)
+        binding.pa_swap_blocks(dk, dv, hk, hv, pout, binding.PA_SWAP_OUT, stream=s2)
+        torch.cuda.current_stream().wait_stream(s1)
+        torch.cuda.current_stream().wait_stream(s2)
+
+    def ordered():
+        binding.pa_swap_blocks(dk, dv, hk, hv, pin, binding.PA_SWAP_IN)
+        binding.pa_swap_blocks(dk, dv, hk, hv, pout, binding.PA_SWAP_OUT)
+    emit({"both_directions": 2 * n * blk, "concurrent_ms": round(_time_ms(concurrent, reps), 4),
+          "ordered_ms": round(_time_ms(ordered, reps), 4)})
+    del dk, dv, hk, hv
+
+    w = config_workload(2)
+    db = DeviceBatch(w)
+    db.write_history()
+    db.write_new()
+    layers, per = 16, 64
+    free = np.setdiff1d(np.arange(w.num_blocks), np.unique(w.block_tables))
+    hkl = torch.zeros((per,) + tuple(db.k_cache.shape[1:]), dtype=db.k_cache.dtype).pin_memory()
+    hvl = torch.zeros((per,) + tuple(db.v_cache.shape[1:]), dtype=db.v_cache.dtype).pin_memory()
+    plan = [LayerSwap(db.k_cache, db.v_cache, hkl, hvl,
+                      torch.from_numpy(np.stack([np.arange(per), free[l * per:(l + 1) * per]], 1)
+                                       .astype(np.int32))) for l in range(layers)]
+    pipe = LayerSwapPipeline()
+
+    def serial():
+        pipe.start_swap_in(plan)
+        torch.cuda.current_stream().wait_stream(pipe.copy_stream)
+        for _ in range(layers):
+            db.attention()
+
+    def pipelined():
+        pipe.start_swap_in(plan)
+        for l in range(layers):
+            pipe.wait_layer(l)
+            db.attention()
+    one_layer_bytes = per * w.num_kv_heads * w.block_size * w.head_dim * 2 * 2
+    emit({"layers": layers, "swap_in_per_layer_bytes": one_layer_bytes,
+          "attention_per_layer_ms": round(_time_ms(db.attention, reps), 4),
+          "swaps_then_attention_ms": round(_time_ms(serial, reps), 4),
+          "layerwise_pipeline_ms": round(_time_ms(pipelined, reps), 4)})
     return 0
 
 
@@ -416,6 +520,8 @@ def main(argv=None) -> int:
                     help="only measure reference HBM rates (torch sum and copy, pa_copy_blocks)")
     ap.add_argument("--paging", action="store_true",
                     help="paging diagnostics: block sizes, contiguous vs shuffled, copy-out, unified vs split calls")
+    ap.add_argument("--swap", action="store_true",
+                    help="host<->device block swap rates and the layer-wise swap-in pipeline, then exit")
     ap.add_argument("--chunk-cost", action="store_true",
                     help="time one 32-token chunk (and 16 of them) after 0..32K cached tokens, then exit")
     ap.add_argument("--mfma-reference", action="store_true",
@@ -445,6 +551,8 @@ def main(argv=None) -> int:
         return chunk_cost(args)
     if args.paging:
         return paging(args)
+    if args.swap:
+        return swap(args)
     t0 = time.time()
     w = config_workload(args.config, args.seed)
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)

@@ -155,6 +155,57 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* c,
                          const int32_t* block_pairs, int32_t num_pairs, hipStream_t stream);
 
 /*
+ * pa_copy_blocks_layers -- the copies of pa_copy_blocks on every layer's pools
+ * in one launch.
+ *
+ * vLLM-SOSP23 page (Kernel 层实现): the copy-on-write block copies are
+ * batched into one kernel; a model keeps one pool pair per layer and the same
+ * block ids in each, so one launch serves all layers.
+ *
+ *  k_caches, v_caches  HOST arrays of num_layers device pool pointers (read
+ *                      during the call, may be freed after it); every layer's
+ *                      pools have the shape and dtype of *c.
+ *  num_layers          0..PA_MAX_LAYERS; more layers take several calls.
+ *  block_pairs, num_pairs, precondition, bounds and exactness as for
+ *  pa_copy_blocks, applied to each layer.
+ */
+#define PA_MAX_LAYERS 128
+pa_status pa_copy_blocks_layers(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                                const pa_cache_desc* c, const int32_t* block_pairs,
+                                int32_t num_pairs, hipStream_t stream);
+
+/*
+ * pa_swap_blocks -- move whole blocks between the device pool and a host pool.
+ *
+ * Pensieve page (流水线KV缓存恢复, 提前交换, 实现细节与优化): K/V tokens evicted
+ * from GPU memory live in a CPU cache and are copied back before the layer
+ * that needs them runs; vLLM-SOSP23 page (调度与抢占): preempted sequences'
+ * blocks are swapped to CPU memory and back.  Runs of consecutive block
+ * pairs are merged; up to 8 runs go to the DMA engines (hipMemcpyAsync on
+ * `stream`, leaving the compute units free), more runs to a copy kernel on
+ * `stream` that addresses the pinned host pool directly (each DMA transfer
+ * has a fixed submission cost).
+ *
+ *  dev_k, dev_v     device pools, layout and shape of *c.
+ *  host_k, host_v   host pools with the same per-block layout and
+ *                   host_num_blocks blocks; pinned (hipHostMalloc, or torch
+ *                   pin_memory=True).  Unpinned memory takes the DMA path
+ *                   with synchronous copies.
+ *  block_pairs      HOST int32 [num_pairs][2] = (src, dst), read during the
+ *                   call: PA_SWAP_OUT copies device block src to host block
+ *                   dst, PA_SWAP_IN host block src to device block dst.  Ids
+ *                   outside their pool give PA_ERR_BOUNDS and nothing is
+ *                   enqueued.  Destinations must be distinct.  Bit-exact.
+ *  direction        PA_SWAP_OUT or PA_SWAP_IN.
+ * The caller orders swaps against attention with events (the page gates each
+ * layer's attention on the event that ends its swap-in).
+ */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+pa_status pa_swap_blocks(void* dev_k, void* dev_v, const pa_cache_desc* c, void* host_k,
+                         void* host_v, int32_t host_num_blocks, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t direction, hipStream_t stream);
+
+/*
  * pa_attention_workspace_size -- bytes of device workspace pa_attention needs
  * for a batch of num_seqs sequences, total_q query rows, and no context longer
  * than max_context_len, with the given options (NULL = defaults).

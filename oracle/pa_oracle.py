@@ -70,6 +70,21 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> None:
         v_cache[dst] = v_cache[src]
 
 
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                pairs) -> None:
+    """Copy whole blocks from one pool pair into another, for each ``(src, dst)``.
+
+    Pensieve page, "流水线KV缓存恢复" and "提前交换": K/V tokens are copied
+    from the GPU cache to a CPU cache (swap-out) and back (swap-in) a block of
+    tokens at a time; vLLM wiki page, "调度与抢占": preempted sequences' blocks
+    are swapped between GPU and CPU memory.  The copy is bitwise; the two pools
+    have the same per-block layout and may differ in block count.
+    """
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+
+
 # --------------------------------------------------------------------------
 # a2: slot-mapping scatter of new K/V
 # --------------------------------------------------------------------------

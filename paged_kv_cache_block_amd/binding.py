@@ -18,8 +18,10 @@ PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
           -4: "PA_ERR_HIP", -5: "PA_ERR_BOUNDS"}
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
-SYMBOLS = ("pa_write_kv", "pa_copy_blocks", "pa_attention_workspace_size", "pa_attention",
-           "pa_last_error", "pa_version")
+SYMBOLS = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks",
+           "pa_attention_workspace_size", "pa_attention", "pa_last_error", "pa_version")
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
+MAX_LAYERS = 128
 
 
 class PaCacheDesc(ctypes.Structure):
@@ -57,6 +59,10 @@ def _load() -> ctypes.CDLL:
     lib.pa_write_kv.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [vp, vp, desc_p, i32p, i32, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_copy_blocks_layers.argtypes = [vp, vp, i32, desc_p, i32p, i32, vp]
+    lib.pa_copy_blocks_layers.restype = ctypes.c_int
+    lib.pa_swap_blocks.argtypes = [vp, vp, desc_p, vp, vp, i32, i32p, i32, i32, vp]
+    lib.pa_swap_blocks.restype = ctypes.c_int
     lib.pa_attention_workspace_size.argtypes = [desc_p, i32, i32, i32, i32, opt_p]
     lib.pa_attention_workspace_size.restype = ctypes.c_size_t
     lib.pa_attention.argtypes = [vp, vp, vp, vp, desc_p, i32, i32p, i32, i32p, i32p, i32, i32,
@@ -127,6 +133,47 @@ def pa_write_kv(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> No
         raise ValueError("slot_mapping must be int64 [T]")
     _check(LIB.pa_write_kv(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), t, _ptr(k_cache),
                            _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
+
+
+def pa_copy_blocks_layers(k_caches, v_caches, block_pairs, stream=None) -> None:
+    """The block copies of ``pa_copy_blocks`` on every layer's pools, one launch."""
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("one K and one V pool per layer")
+    desc = cache_desc(k_caches[0], v_caches[0])
+    for k, v in zip(k_caches, v_caches):
+        if tuple(k.shape) != tuple(k_caches[0].shape) or k.dtype != k_caches[0].dtype or \
+                tuple(v.shape) != tuple(v_caches[0].shape):
+            raise ValueError("every layer's pools must have the same shape and dtype")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int32 [n][2]")
+    n = len(k_caches)
+    kp = (ctypes.c_void_p * n)(*[_ptr(k) for k in k_caches])
+    vp_ = (ctypes.c_void_p * n)(*[_ptr(v) for v in v_caches])
+    _check(LIB.pa_copy_blocks_layers(ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp_, ctypes.c_void_p),
+                                     n, ctypes.byref(desc), _ptr(block_pairs.contiguous()),
+                                     int(block_pairs.shape[0]), _stream(stream)))
+
+
+def pa_swap_blocks(dev_k, dev_v, host_k, host_v, block_pairs, direction: int, stream=None) -> None:
+    """Copy whole blocks device -> host (PA_SWAP_OUT) or host -> device
+    (PA_SWAP_IN) on the DMA engines.  ``host_k`` / ``host_v`` are pinned CPU
+    tensors shaped like the device pools (any block count); ``block_pairs``
+    is an int32 CPU tensor [n][2] of (src, dst)."""
+    desc = cache_desc(dev_k, dev_v)
+    if host_k.device.type != "cpu" or host_v.device.type != "cpu":
+        raise ValueError("host pools must be CPU tensors")
+    if tuple(host_k.shape[1:]) != tuple(dev_k.shape[1:]) or tuple(host_v.shape[1:]) != tuple(dev_v.shape[1:]) \
+            or host_k.dtype != dev_k.dtype or host_v.dtype != dev_v.dtype or host_k.shape[0] != host_v.shape[0]:
+        raise ValueError("host pools must match the device pools' block shape and dtype")
+    if not (host_k.is_contiguous() and host_v.is_contiguous()):
+        raise ValueError("host pools must be contiguous")
+    if block_pairs.device.type != "cpu" or block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 \
+            or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be an int32 CPU tensor [n][2]")
+    pairs = block_pairs.contiguous()
+    _check(LIB.pa_swap_blocks(_ptr(dev_k), _ptr(dev_v), ctypes.byref(desc), _ptr(host_k), _ptr(host_v),
+                              int(host_k.shape[0]), _ptr(pairs), int(pairs.shape[0]), int(direction),
+                              _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:

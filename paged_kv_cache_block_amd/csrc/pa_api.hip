@@ -198,6 +198,114 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const pa_cache_desc* c,
   return e == hipSuccess ? PA_OK : hip_fail(e, "copy_blocks launch");
 }
 
+pa_status pa_swap_blocks(void* dev_k, void* dev_v, const pa_cache_desc* c, void* host_k,
+                         void* host_v, int32_t host_num_blocks, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t direction, hipStream_t stream) {
+  PoolArgs p;
+  pa_status st = check_desc(c, &p);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || host_num_blocks < 0) return fail(PA_ERR_INVALID_ARG, "negative count");
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID_ARG, "direction must be PA_SWAP_OUT or PA_SWAP_IN");
+  if (num_pairs == 0) return PA_OK;
+  if (!dev_k || !dev_v || !host_k || !host_v || !block_pairs)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  const bool out = direction == PA_SWAP_OUT;
+  const int64_t src_n = out ? p.num_blocks : host_num_blocks;
+  const int64_t dst_n = out ? host_num_blocks : p.num_blocks;
+  std::vector<int32_t> dsts;
+  dsts.reserve(num_pairs);
+  for (int i = 0; i < num_pairs; ++i) {
+    const int32_t a = block_pairs[2 * i], b = block_pairs[2 * i + 1];
+    if (a < 0 || a >= src_n || b < 0 || b >= dst_n)
+      return fail(PA_ERR_BOUNDS, "swap pair (%d, %d) out of range", a, b);
+    dsts.push_back(b);
+  }
+  std::sort(dsts.begin(), dsts.end());
+  if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end())
+    return fail(PA_ERR_BOUNDS, "duplicate destination block");
+  const size_t blk = (size_t)p.num_kv_heads * p.block_size * p.head_dim * (p.dtype == DT_F32 ? 4 : 2);
+  char* sk = static_cast<char*>(out ? dev_k : host_k);
+  char* sv = static_cast<char*>(out ? dev_v : host_v);
+  char* dk = static_cast<char*>(out ? host_k : dev_k);
+  char* dv = static_cast<char*>(out ? host_v : dev_v);
+  const hipMemcpyKind kind = out ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  // Runs of pairs whose sources and destinations both advance by one block
+  // become one DMA transfer each for K and for V.  Many short runs instead go
+  // through a copy kernel that addresses the (pinned, mapped) host pool
+  // directly, since each DMA transfer costs a fixed submission time.
+  int runs = 0;
+  for (int i = 0; i < num_pairs; ++runs) {
+    int run = 1;
+    while (i + run < num_pairs && block_pairs[2 * (i + run)] == block_pairs[2 * i] + run &&
+           block_pairs[2 * (i + run) + 1] == block_pairs[2 * i + 1] + run)
+      ++run;
+    i += run;
+  }
+  void* hk_dev = nullptr;
+  void* hv_dev = nullptr;
+  if (runs > kSwapDmaMaxRuns && hipHostGetDevicePointer(&hk_dev, host_k, 0) == hipSuccess &&
+      hipHostGetDevicePointer(&hv_dev, host_v, 0) == hipSuccess) {
+    const void* s_k = out ? dev_k : hk_dev;
+    const void* s_v = out ? dev_v : hv_dev;
+    void* d_k = out ? hk_dev : dev_k;
+    void* d_v = out ? hv_dev : dev_v;
+    for (int i0 = 0; i0 < num_pairs; i0 += kSwapPairsPerLaunch) {
+      const int n = std::min(kSwapPairsPerLaunch, num_pairs - i0);
+      SwapPairs sp;
+      memcpy(sp.p, block_pairs + 2 * i0, sizeof(int32_t) * 2 * n);
+      const hipError_t e = launch_swap_kernel(s_k, s_v, d_k, d_v, p, sp, n, stream);
+      if (e != hipSuccess) return hip_fail(e, "swap kernel launch");
+    }
+    return PA_OK;
+  }
+  (void)hipGetLastError();   // clear a failed pointer query (memory not mapped)
+  for (int i = 0; i < num_pairs;) {
+    const int32_t a = block_pairs[2 * i], b = block_pairs[2 * i + 1];
+    int run = 1;
+    while (i + run < num_pairs && block_pairs[2 * (i + run)] == a + run &&
+           block_pairs[2 * (i + run) + 1] == b + run)
+      ++run;
+    hipError_t e = hipMemcpyAsync(dk + (size_t)b * blk, sk + (size_t)a * blk, run * blk, kind, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(dv + (size_t)b * blk, sv + (size_t)a * blk, run * blk, kind, stream);
+    if (e != hipSuccess) return hip_fail(e, "swap copy");
+    i += run;
+  }
+  return PA_OK;
+}
+
+static_assert(kMaxLayers == PA_MAX_LAYERS, "layer limit of the ABI and the kernel arguments");
+
+pa_status pa_copy_blocks_layers(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                                const pa_cache_desc* c, const int32_t* block_pairs,
+                                int32_t num_pairs, hipStream_t stream) {
+  PoolArgs p;
+  pa_status st = check_desc(c, &p);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_layers < 0) return fail(PA_ERR_INVALID_ARG, "negative count");
+  if (num_layers > PA_MAX_LAYERS)
+    return fail(PA_ERR_INVALID_ARG, "%d layers in one call, at most %d", num_layers, PA_MAX_LAYERS);
+  if (num_pairs == 0 || num_layers == 0) return PA_OK;
+  if (!k_caches || !v_caches || !block_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  LayerPools lp{};
+  for (int l = 0; l < num_layers; ++l) {
+    if (!k_caches[l] || !v_caches[l]) return fail(PA_ERR_INVALID_ARG, "null pool of layer %d", l);
+    if (!aligned16(k_caches[l]) || !aligned16(v_caches[l]))
+      return fail(PA_ERR_INVALID_ARG, "pools of layer %d must be 16-byte aligned", l);
+    lp.k[l] = k_caches[l];
+    lp.v[l] = v_caches[l];
+  }
+  if (validate_mode()) {
+    std::vector<int32_t> pr;
+    if ((st = fetch(pr, block_pairs, 2 * (size_t)num_pairs, stream)) != PA_OK) return st;
+    for (int i = 0; i < num_pairs; ++i)
+      if (pr[2 * i] < 0 || pr[2 * i] >= p.num_blocks || pr[2 * i + 1] < 0 || pr[2 * i + 1] >= p.num_blocks)
+        return fail(PA_ERR_BOUNDS, "block pair (%d, %d) out of range", pr[2 * i], pr[2 * i + 1]);
+  }
+  hipError_t e = launch_copy_blocks_layers(lp, num_layers, p, block_pairs, num_pairs, stream);
+  return e == hipSuccess ? PA_OK : hip_fail(e, "copy_blocks_layers launch");
+}
+
 size_t pa_attention_workspace_size(const pa_cache_desc* c, int32_t num_q_heads, int32_t num_seqs,
                                    int32_t total_q, int32_t max_context_len,
                                    const pa_options* opt) {

@@ -53,6 +53,24 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, const int64_t* 
                            hipStream_t s);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const PoolArgs& p,
                               const int32_t* pairs, int num_pairs, hipStream_t s);
+// Pool pointers of every layer, passed by value to the multi-layer copy.
+constexpr int kMaxLayers = 128;
+struct LayerPools {
+  void* k[kMaxLayers];
+  void* v[kMaxLayers];
+};
+hipError_t launch_copy_blocks_layers(const LayerPools& lp, int num_layers, const PoolArgs& p,
+                                     const int32_t* pairs, int num_pairs, hipStream_t s);
+// Block copies between a device pool and a host pool the device can address
+// (pinned, mapped): the pairs travel in the kernel arguments.
+constexpr int kSwapPairsPerLaunch = 448;
+// Swaps with more runs of consecutive blocks than this use the copy kernel.
+constexpr int kSwapDmaMaxRuns = 8;
+struct SwapPairs {
+  int32_t p[2 * kSwapPairsPerLaunch];
+};
+hipError_t launch_swap_kernel(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const PoolArgs& p, const SwapPairs& pairs, int n, hipStream_t s);
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* qsl, const PlanParams& pp,
                        void* ws, const WorkspaceLayout& lay, hipStream_t s);
 

@@ -92,7 +92,86 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   }
 }
 
+// The copies of pa_copy_blocks on every layer's pools: grid.z is the layer,
+// whose pool pointers travel in the kernel arguments.
+__global__ __launch_bounds__(256) void copy_blocks_layers_kernel(LayerPools lp,
+                                                                 const int32_t* __restrict__ pairs,
+                                                                 int64_t chunks_per_block,
+                                                                 int num_blocks) {
+  uint4* k_cache = reinterpret_cast<uint4*>(lp.k[blockIdx.z]);
+  uint4* v_cache = reinterpret_cast<uint4*>(lp.v[blockIdx.z]);
+  const int p = blockIdx.x;
+  const int src = pairs[2 * p];
+  const int dst = pairs[2 * p + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t s0 = (int64_t)src * chunks_per_block;
+  const int64_t d0 = (int64_t)dst * chunks_per_block;
+  for (int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x; c < chunks_per_block;
+       c += (int64_t)gridDim.y * 256) {
+    const uint4 a = k_cache[s0 + c];
+    const uint4 b = v_cache[s0 + c];
+    k_cache[d0 + c] = a;
+    v_cache[d0 + c] = b;
+  }
+}
+
+// Whole-block copies between two pools, one of them host memory mapped into
+// the device's address space.  Each thread moves four 16-byte chunks of K and
+// four of V, loads first, so that eight transfers over the host link are in
+// flight per thread.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const uint4* __restrict__ src_k,
+                                                          const uint4* __restrict__ src_v,
+                                                          uint4* __restrict__ dst_k,
+                                                          uint4* __restrict__ dst_v, SwapPairs pairs,
+                                                          int64_t chunks_per_block) {
+  const int i = blockIdx.x;
+  const int64_t s0 = (int64_t)pairs.p[2 * i] * chunks_per_block;
+  const int64_t d0 = (int64_t)pairs.p[2 * i + 1] * chunks_per_block;
+  const int64_t c0 = (int64_t)blockIdx.y * 1024 + threadIdx.x;
+  if (c0 + 768 < chunks_per_block) {
+    uint4 k[4], v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      k[u] = src_k[s0 + c0 + 256 * u];
+      v[u] = src_v[s0 + c0 + 256 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      dst_k[d0 + c0 + 256 * u] = k[u];
+      dst_v[d0 + c0 + 256 * u] = v[u];
+    }
+    return;
+  }
+  for (int64_t c = c0; c < chunks_per_block; c += 256) {   // a block's last partial slice
+    dst_k[d0 + c] = src_k[s0 + c];
+    dst_v[d0 + c] = src_v[s0 + c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swap_kernel(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const PoolArgs& p, const SwapPairs& pairs, int n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int eb = p.dtype == DT_F32 ? 4 : 2;
+  const int64_t cpb = (int64_t)p.num_kv_heads * p.block_size * p.head_dim * eb / 16;
+  const dim3 grid(n, (unsigned)((cpb + 1023) / 1024));
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(256), 0, s, (const uint4*)src_k,
+                     (const uint4*)src_v, (uint4*)dst_k, (uint4*)dst_v, pairs, cpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks_layers(const LayerPools& lp, int num_layers, const PoolArgs& p,
+                                     const int32_t* pairs, int num_pairs, hipStream_t s) {
+  if (num_pairs == 0 || num_layers == 0) return hipSuccess;
+  const int eb = p.dtype == DT_F32 ? 4 : 2;
+  const int64_t cpb = (int64_t)p.num_kv_heads * p.block_size * p.head_dim * eb / 16;
+  int gy = (int)((cpb + 255) / 256);
+  if (gy > 64) gy = 64;
+  hipLaunchKernelGGL(copy_blocks_layers_kernel, dim3(num_pairs, gy, num_layers), dim3(256), 0, s,
+                     lp, pairs, cpb, p.num_blocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int64_t* slots,
                            int num_tokens, void* k_cache, void* v_cache, const PoolArgs& p,

@@ -117,6 +117,47 @@ def test_write_and_copy_argument_errors(binding):
     assert b.LIB.pa_copy_blocks(16, 16, ctypes.byref(desc), 16, 1, None) == -2
 
 
+def test_copy_blocks_layers_argument_errors(binding):
+    b = binding
+    desc = _desc(b)
+    lib = b.LIB
+    ptrs = (ctypes.c_void_p * 200)(*([1 << 20] * 200))
+    arr = ctypes.cast(ptrs, ctypes.c_void_p)
+    assert lib.pa_copy_blocks_layers(arr, arr, 0, ctypes.byref(desc), 16, 3, None) == 0     # no layers
+    assert lib.pa_copy_blocks_layers(arr, arr, 4, ctypes.byref(desc), 16, 0, None) == 0     # no pairs
+    assert lib.pa_copy_blocks_layers(arr, arr, 129, ctypes.byref(desc), 16, 3, None) == -1  # > 128 layers
+    assert lib.pa_copy_blocks_layers(None, arr, 2, ctypes.byref(desc), 16, 3, None) == -1
+    assert lib.pa_copy_blocks_layers(arr, arr, 2, ctypes.byref(desc), None, 3, None) == -1
+    assert lib.pa_copy_blocks_layers(arr, arr, 2, ctypes.byref(desc), 16, -1, None) == -1
+    bad = (ctypes.c_void_p * 2)(1 << 20, 8)                                       # misaligned layer 1
+    assert lib.pa_copy_blocks_layers(ctypes.cast(bad, ctypes.c_void_p), arr, 2, ctypes.byref(desc),
+                                     16, 3, None) == -1
+    desc.block_size = 3
+    assert lib.pa_copy_blocks_layers(arr, arr, 2, ctypes.byref(desc), 16, 3, None) == -2
+    assert b.MAX_LAYERS == 128
+
+
+def test_swap_blocks_argument_errors(binding):
+    b = binding
+    desc = _desc(b)                       # 16 device blocks
+    lib = b.LIB
+
+    def call(pairs, direction=0, host_blocks=8, n=None):
+        arr = (ctypes.c_int32 * max(1, 2 * len(pairs)))(*[x for p in pairs for x in p])
+        n = len(pairs) if n is None else n
+        return lib.pa_swap_blocks(1 << 20, 1 << 20, ctypes.byref(desc), 1 << 21, 1 << 21, host_blocks,
+                                  ctypes.cast(arr, ctypes.c_void_p), n, direction, None)
+    assert call([]) == 0                                   # nothing to do
+    assert call([(1, 2)], direction=2) == -1               # unknown direction
+    assert call([(16, 2)], direction=0) == -5              # device block out of range (swap-out source)
+    assert call([(1, 8)], direction=0) == -5               # host block out of range
+    assert call([(8, 1)], direction=1) == -5               # host source out of range (swap-in)
+    assert call([(1, 3), (2, 3)], direction=0) == -5       # duplicate destination
+    assert call([(1, 2)], n=-1) == -1
+    assert lib.pa_swap_blocks(None, 1 << 20, ctypes.byref(desc), 1 << 21, 1 << 21, 8,
+                              ctypes.cast((ctypes.c_int32 * 2)(1, 2), ctypes.c_void_p), 1, 0, None) == -1
+
+
 def test_empty_batch_is_ok_without_a_gpu(binding):
     b = binding
     desc = _desc(b)

@@ -3,6 +3,9 @@
 Bars: scatter, block copy and indexing bit-exact; attention within
 max |d| <= 1e-5 for fp32 inputs, and max |d| <= 1e-2 with mean |d| <= 1e-3
 for fp16 / bf16 inputs (fp32 accumulation on the GPU, float64 in the oracle).
+The output is rounded once to its 16-bit type, which alone moves a bf16
+value of magnitude |o| by up to 2^-8 |o| (more than 1e-2 above |o| = 2.56),
+so for 16-bit outputs the 1e-2 bound is taken relative to max(1, |o|).
 """
 import os
 import sys
@@ -51,8 +54,10 @@ def compare(got_storage, want64, dtype, rows=None, what=""):
     diff = np.abs(got - want64)
     mx, mean = float(diff.max()), float(diff.mean())
     tmax, tmean = TOL[dtype]
-    say(f"{what}: max|d|={mx:.3e} mean|d|={mean:.3e}")
-    assert mx <= tmax, f"{what}: max |d| {mx} > {tmax}"
+    scale = np.maximum(1.0, np.abs(want64)) if dtype != "f32" else 1.0
+    worst = float((diff / scale).max())
+    say(f"{what}: max|d|={mx:.3e} max|d|/max(1,|o|)={worst:.3e} mean|d|={mean:.3e}")
+    assert worst <= tmax, f"{what}: max |d| / max(1, |o|) = {worst} > {tmax}"
     assert mean <= tmean, f"{what}: mean |d| {mean} > {tmean}"
 
 
@@ -80,6 +85,116 @@ def test_write_and_copy_bit_exact(torch_cuda, cfg):
     k, v = oracle_step(w)
     assert np.array_equal(bits(gk), bits(k)), "K pool differs"
     assert np.array_equal(bits(gv), bits(v)), "V pool differs"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_copy_blocks_layers_bit_exact(torch_cuda, dtype):
+    """One launch applies the same copy-on-write pairs to every layer's pools."""
+    torch = torch_cuda
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.step import TORCH_DTYPE, to_numpy, to_torch
+    from workloads import round_to_dtype
+    nb, h, bs, d, layers = 40, 2, 16, 64, 5
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:12], perm[12:24]], 1).astype(np.int32)    # distinct, disjoint
+    ks, vs, want = [], [], []
+    for l in range(layers):
+        k = round_to_dtype(rng.standard_normal((nb, h, bs, d), dtype=np.float32), dtype)
+        v = round_to_dtype(rng.standard_normal((nb, h, d, bs), dtype=np.float32), dtype)
+        ks.append(to_torch(k, dtype, "cuda"))
+        vs.append(to_torch(v, dtype, "cuda"))
+        k2, v2 = k.copy(), v.copy()
+        oracle.copy_blocks(k2, v2, pairs)
+        want.append((k2, v2))
+    say("copy layers", dtype)
+    binding.pa_copy_blocks_layers(ks, vs, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    for l in range(layers):
+        assert np.array_equal(bits(to_numpy(ks[l], dtype)), bits(want[l][0])), l
+        assert np.array_equal(bits(to_numpy(vs[l], dtype)), bits(want[l][1])), l
+
+
+@pytest.mark.parametrize("dtype,scattered", [("bf16", False), ("f32", False), ("bf16", True), ("f16", True)])
+def test_swap_out_and_in_bit_exact(torch_cuda, dtype, scattered):
+    """Blocks go to a pinned host pool and come back into other device
+    blocks: a few runs (DMA engines) or many scattered pairs (the copy kernel
+    over the host link), bit-exact."""
+    torch = torch_cuda
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.step import TORCH_DTYPE, to_numpy, to_torch
+    from workloads import round_to_dtype
+    nb, hnb, h, bs, d = 48, 40, 2, 16, 64
+    rng = np.random.default_rng(17)
+    k = round_to_dtype(rng.standard_normal((nb, h, bs, d), dtype=np.float32), dtype)
+    v = round_to_dtype(rng.standard_normal((nb, h, d, bs), dtype=np.float32), dtype)
+    dk, dv = to_torch(k, dtype, "cuda"), to_torch(v, dtype, "cuda")
+    dt = TORCH_DTYPE[dtype]
+    hk = torch.zeros((hnb, h, bs, d), dtype=dt).pin_memory()
+    hv = torch.zeros((hnb, h, d, bs), dtype=dt).pin_memory()
+    if scattered:      # 20 pairs, no two consecutive: 20 runs
+        src = rng.permutation(nb)[:20]
+        hdst = rng.permutation(hnb)[:20]
+        out_pairs = np.stack([src, hdst], 1).astype(np.int32)
+        in_pairs = np.stack([hdst, rng.permutation(nb)[:20]], 1).astype(np.int32)
+    else:
+        out_pairs = np.array([[5, 10], [6, 11], [7, 12], [30, 0], [2, 39], [3, 20]], dtype=np.int32)
+        in_pairs = np.array([[10, 40], [11, 41], [12, 42], [0, 44], [39, 47], [20, 45]], dtype=np.int32)
+    say("swap", dtype)
+    binding.pa_swap_blocks(dk, dv, hk, hv, torch.from_numpy(out_pairs), binding.PA_SWAP_OUT)
+    binding.pa_swap_blocks(dk, dv, hk, hv, torch.from_numpy(in_pairs), binding.PA_SWAP_IN)
+    torch.cuda.synchronize()
+    wk, wv = k.copy(), v.copy()
+    whk = np.zeros_like(to_numpy(hk, dtype))
+    whv = np.zeros_like(to_numpy(hv, dtype))
+    oracle.swap_blocks(wk, wv, whk, whv, out_pairs)
+    oracle.swap_blocks(whk, whv, wk, wv, in_pairs)
+    assert np.array_equal(bits(to_numpy(hk, dtype)), bits(whk))
+    assert np.array_equal(bits(to_numpy(hv, dtype)), bits(whv))
+    assert np.array_equal(bits(to_numpy(dk, dtype)), bits(wk))
+    assert np.array_equal(bits(to_numpy(dv, dtype)), bits(wv))
+
+
+def test_layerwise_swap_in_gates_attention(torch_cuda):
+    """Three layers whose history blocks were swapped out (device copies then
+    poisoned) are swapped back in on a copy stream; each layer's attention
+    waits only for its own layer's event and still matches the oracle."""
+    torch = torch_cuda
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.swap import LayerSwap, LayerSwapPipeline
+    layers, swaps, wants, dbs = 3, [], [], []
+    for l in range(layers):
+        w = small_workload(5, 500 + l)
+        db = run_gpu(w)                            # history + step written, pools complete
+        k, v = oracle_step(w)
+        wants.append(oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                                      w.num_kv_heads, w.dtype, w.scale))
+        used = np.unique(np.concatenate([w.block_tables[s, :-(-int(L) // w.block_size)]
+                                         for s, L in enumerate(w.context_lens)]))
+        moved = used[::2].astype(np.int32)          # every other live block goes to the host
+        hk = torch.empty((moved.size,) + tuple(db.k_cache.shape[1:]), dtype=db.k_cache.dtype).pin_memory()
+        hv = torch.empty((moved.size,) + tuple(db.v_cache.shape[1:]), dtype=db.v_cache.dtype).pin_memory()
+        out_pairs = torch.from_numpy(np.stack([moved, np.arange(moved.size, dtype=np.int32)], 1))
+        binding.pa_swap_blocks(db.k_cache, db.v_cache, hk, hv, out_pairs, binding.PA_SWAP_OUT)
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(moved.astype(np.int64)).cuda()
+        db.k_cache.index_fill_(0, idx, float("nan"))
+        db.v_cache.index_fill_(0, idx, float("nan"))
+        in_pairs = torch.from_numpy(np.stack([np.arange(moved.size, dtype=np.int32), moved], 1))
+        swaps.append(LayerSwap(db.k_cache, db.v_cache, hk, hv, in_pairs))
+        dbs.append(db)
+    torch.cuda.synchronize()
+    say("layerwise swap-in")
+    pipe = LayerSwapPipeline()
+    pipe.start_swap_in(swaps)
+    outs = []
+    for l in range(layers):
+        pipe.wait_layer(l)
+        outs.append(dbs[l].attention(out=torch.empty_like(dbs[l].q)))
+    torch.cuda.synchronize()
+    from paged_kv_cache_block_amd.step import to_numpy
+    for l in range(layers):
+        compare(to_numpy(outs[l], dbs[l].w.dtype), wants[l], dbs[l].w.dtype, what=f"layer {l} after swap-in")
 
 
 @pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 32), ("f32", 8), ("f16", 128)])

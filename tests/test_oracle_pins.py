@@ -330,3 +330,25 @@ def test_unused_slots_never_reach_the_output():
         rows = out[~np.isnan(out).all(axis=(1, 2))]
         assert rows.shape[0] == out.shape[0]
         assert np.isfinite(out).all()
+
+
+def test_swap_out_then_in_restores_the_pool_and_matches_copy_blocks():
+    """Swapping blocks to a second pool and back is the identity on those
+    blocks; within one pool it is exactly the copy-on-write copy."""
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((12, 2, 4, 8))
+    v = rng.standard_normal((12, 2, 8, 4))
+    hk, hv = np.zeros((5, 2, 4, 8)), np.zeros((5, 2, 8, 4))
+    out_pairs = [(3, 0), (7, 4), (8, 1)]
+    oracle.swap_blocks(k, v, hk, hv, out_pairs)
+    assert np.array_equal(hk[[0, 4, 1]], k[[3, 7, 8]]) and np.array_equal(hv[4], v[7])
+    assert not hk[[2, 3]].any()                 # untouched host blocks stay as they were
+    k2, v2 = k.copy(), v.copy()
+    k2[[3, 7, 8]] = 0
+    v2[[3, 7, 8]] = 0
+    oracle.swap_blocks(hk, hv, k2, v2, [(s, d) for d, s in out_pairs])
+    assert np.array_equal(k2, k) and np.array_equal(v2, v)
+    k3, v3, k4, v4 = k.copy(), v.copy(), k.copy(), v.copy()
+    oracle.swap_blocks(k3, v3, k3, v3, [(1, 9), (2, 10)])
+    oracle.copy_blocks(k4, v4, [(1, 9), (2, 10)])
+    assert np.array_equal(k3, k4) and np.array_equal(v3, v4)
