@@ -12,14 +12,17 @@
 //   S^T[key][head]  = K[key][:] . Q[head][:]      v_mfma_f32_16x16x32_{f16,bf16}
 //   online softmax per head (a head is one lane column of S^T)
 //   O^T[d][head]   += V^T[d][key] . P^T[key][head]
-// Both MFMA A operands are read straight from HBM into registers:
-//   K is token-major, so lane (row r, k-group c) loads 16 bytes of one key row;
-//   V is head-dim-major inside a block, so lane (row d, k-group c) loads the
-//   8 consecutive keys 8c..8c+7 of head-dim row d.
+// The V^T operand is read straight from HBM into registers: V is head-dim-
+// major inside a block, so lane (row d, k-group c) loads the 8 consecutive
+// keys 8c..8c+7 of head-dim row d.  K (token-major) is read as contiguous
+// 1 KB pieces, each lane one 16-byte chunk, and reaches the operand layout
+// (lane (row r, k-group c): 16 bytes of key row r) through LDS.
 // The K rows are permuted so the four S^T values a lane gets from each of the
 // two key tiles are exactly the 8 consecutive keys its P^T operand needs.
 // Keys go 32 per step, double-buffered: the next step's K and V loads are in
-// flight while the current step computes.  No LDS is used.
+// flight while the current step computes.  K rows are loaded as contiguous
+// 1 KB pieces and pass through 8 KB of LDS per wave to reach the operand
+// layout.
 
 #include "pa_internal.h"
 
@@ -68,12 +71,21 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 
 template <int D>
 struct Stage {
-  u32x4 k[2][D / 32];   // two 16-key tiles x (D/32) k-steps
+  u32x4 k[D / 16];      // the step's 32 K rows, as D/16 contiguous 1 KB pieces
   u32x4 v[D / 16];      // D/16 head-dim tiles, 8 keys each
 };
 
+// Position of 16-byte chunk j of key row r (0..31) in a wave's LDS copy of a
+// step's K rows: rows of 2D bytes, chunks XOR-swizzled by row so that the
+// operand reads (16 rows, one chunk) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int kslot(int r, int j) {
+  const int sw = D == 128 ? ((r & 3) | (((r >> 3) & 3) << 2)) : ((r & 3) | (((r >> 3) & 1) << 2));
+  return r * (D / 8) + (j ^ sw);
+}
+
 template <int DT, int D, int BS, bool NT>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
+__global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
                                                          WorkspaceLayout lay, int split_tokens) {
   constexpr int KS = D / 32;
   constexpr int NDT = D / 16;
@@ -122,20 +134,24 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
   // 8*(c16>>2) + 4u + (c16&3); lane group grp's V operand holds keys 8grp..8grp+7.
   const int krow0 = 8 * (c16 >> 2) + (c16 & 3);
   const int vkey = 8 * grp;
+  // K is loaded as contiguous 1 KB pieces (piece i: keys KPI*i .. +KPI, lane
+  // = 16-byte chunk; reads shaped so stream faster than 64-byte row pieces)
+  // and rearranged into the MFMA operand layout through LDS.
+  constexpr int CPRW = D / 8;          // 16-byte chunks per K row
+  constexpr int KPI = 64 / CPRW;       // keys per 1 KB piece
+  __shared__ __attribute__((aligned(16))) u32x4 kl[32 * CPRW];
+  const int pkey = lane / CPRW, pchunk = lane % CPRW;
 
   auto load = [&](int c0, Stage<D>& st) {
     const unsigned b0 = min((unsigned)bt[min(c0 / BS, tb_max)], nb_max);
     unsigned b1 = b0;
     if constexpr (BS == 16) b1 = min((unsigned)bt[min(c0 / BS + 1, tb_max)], nb_max);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = krow0 + 4 * u;                       // 0..31
+    for (int i = 0; i < D / 16; ++i) {
+      const int kk = KPI * i + pkey;                      // 0..31
       const unsigned blk = (BS == 16 && kk >= 16) ? b1 : b0;
       const int off = (c0 + kk) % BS;
-      const uint16_t* kp = kc + (((int64_t)blk * Hkv + g) * BS + off) * D + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        st.k[u][ks] = ld16<NT>(kp + 32 * ks);
+      st.k[i] = ld16<NT>(kc + (((int64_t)blk * Hkv + g) * BS + off) * D + 8 * pchunk);
     }
     {
       const unsigned blk = (BS == 16 && vkey >= 16) ? b1 : b0;
@@ -153,12 +169,21 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(AttnArgs a, PoolArgs p,
   float m_run = -INFINITY, l_run = 0.f;
 
   auto compute = [&](int c0, Stage<D>& st) {
+    // K pieces to LDS, then the operands back in MFMA layout (one wave per
+    // workgroup: the LDS ops of a wave complete in order, so no barrier).
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) kl[kslot<D>(KPI * i + pkey, pchunk)] = st.k[i];
+    u32x4 kop[2][KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kop[u][ks] = kl[kslot<D>(krow0 + 4 * u, 4 * ks + grp)];
     f32x4 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc[u] = mfma16<DT>(st.k[u][ks], qreg[ks], sacc[u]);
+      for (int ks = 0; ks < KS; ++ks) sacc[u] = mfma16<DT>(kop[u][ks], qreg[ks], sacc[u]);
     }
     // This lane holds head c16's scores for keys c0 + 8grp + (4u + i).
     const bool tail = c0 + 32 > t1;
