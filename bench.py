@@ -4,7 +4,9 @@
 A step is the whole path over one synthetic batch with its inputs resident in
 HBM: copy-on-write block copies, the slot-mapping write of the new tokens,
 and causal paged attention of every query row (plan, multi-token MFMA
-kernel, vector-ALU row kernel, split combine).  The default workload is the
+kernel, decode kernel, split combine).  The write and attention go through
+one pa_write_kv_attention call (the write shares the planner's launch);
+``--separate-write`` times pa_write_kv + pa_attention.  The default workload is the
 64-sequence fp16 decode batch at 40 heads x 128 (block size 16, contexts
 uniform in 128..2048); ``--config`` picks another named workload.
 
@@ -512,6 +514,8 @@ def main(argv=None) -> int:
     ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
     ap.add_argument("--prefill-split", type=int, default=0,
                     help="keys per split of a multi-token context (0 = no split)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="time pa_write_kv then pa_attention instead of pa_write_kv_attention")
     ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 128, 256],
                     help="rows per multi-token MFMA work item (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -577,8 +581,11 @@ def main(argv=None) -> int:
 
     def run_step(opt):
         db.copy_blocks()
-        db.write_new()
-        db.attention(opt=opt)
+        if args.separate_write:
+            db.write_new()
+            db.attention(opt=opt)
+        else:
+            db.write_attention(opt=opt)
 
     base_opt = binding.options(args.split, args.prefill_split, flags, prefill_tile_rows=args.tile_rows)
     for _ in range(args.warmup):
@@ -657,6 +664,8 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "config": args.config, "seqs": w.num_seqs,
                    "query_rows": int(w.q.shape[0]), "new_tokens": int(w.k_new.shape[0]),
                    "cow_pairs": int(w.cow_pairs.shape[0]), "kv_unshared_hint": unshared,
+                   "step": ("pa_copy_blocks, pa_write_kv, pa_attention" if args.separate_write
+                            else "pa_copy_blocks, pa_write_kv_attention"),
                    "step_bytes": model["step_bytes"], "multi_token_flops": model["tile_flops"]},
         "roofline": roof,
         "kernels_ms": {k2: round(v, 5) for k2, v in per_kernel.items()},

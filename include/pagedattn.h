@@ -267,6 +267,39 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
                        float scale, void* workspace, size_t workspace_bytes,
                        const pa_options* opt, hipStream_t stream);
 
+/*
+ * pa_write_kv_attention -- the new tokens' K/V written into the pools, then
+ * attention over them: the result of pa_write_kv(k_new, v_new, slot_mapping,
+ * total_q, ...) followed by pa_attention(...), in one call.
+ *
+ * vLLM-SOSP23 page (Kernel 层实现): the block write of new K/V is fused with
+ * the work around it to save launches.  Pensieve page
+ * (统一Prefill和Generation阶段的执行过程): each batched token's new K/V is
+ * stored into its slot before attention reads it.
+ *
+ * The write shares one launch with the attention planner (neither reads what
+ * the other writes), so the call has one launch fewer than the two calls it
+ * replaces; the attention kernels then read the new tokens from the pools.
+ *
+ *  k_new, v_new    device [total_q][num_kv_heads][head_dim], c->dtype, 16-byte
+ *                  aligned: row t is the K/V of query row t (the new tokens
+ *                  are the queries).
+ *  slot_mapping    device int64 [total_q]; the slot of query row t's token,
+ *                  as for pa_write_kv (its PA_VALIDATE=1 checks included).
+ *  k_cache,v_cache device pools, modified at the new tokens' slots.
+ *  Other arguments, errors and options as for pa_attention.
+ */
+pa_status pa_write_kv_attention(void* out, const void* q, const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                const pa_cache_desc* c, int32_t num_q_heads,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t total_q,
+                                const int32_t* context_lens_host,
+                                const int32_t* query_start_loc_host, float scale,
+                                void* workspace, size_t workspace_bytes, const pa_options* opt,
+                                hipStream_t stream);
+
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* pa_last_error(void);
 

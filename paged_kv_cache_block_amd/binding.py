@@ -68,6 +68,10 @@ def _load() -> ctypes.CDLL:
     lib.pa_attention.argtypes = [vp, vp, vp, vp, desc_p, i32, i32p, i32, i32p, i32p, i32, i32,
                                  i32p, i32p, ctypes.c_float, vp, ctypes.c_size_t, opt_p, vp]
     lib.pa_attention.restype = ctypes.c_int
+    lib.pa_write_kv_attention.argtypes = [vp, vp, vp, vp, i64p, vp, vp, desc_p, i32, i32p, i32,
+                                          i32p, i32p, i32, i32, i32p, i32p, ctypes.c_float, vp,
+                                          ctypes.c_size_t, opt_p, vp]
+    lib.pa_write_kv_attention.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
@@ -192,15 +196,8 @@ def pa_attention_workspace_size(desc: PaCacheDesc, num_q_heads: int, num_seqs: i
                                                ctypes.byref(opt) if opt is not None else None))
 
 
-def pa_attention(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
-                 context_lens_host, query_start_loc_host, scale: float, workspace,
-                 opt: PaOptions | None = None, stream=None) -> None:
-    """Causal paged attention of a ragged batch; writes ``out`` in place.
-
-    ``context_lens_host`` / ``query_start_loc_host`` are contiguous int32 CPU
-    tensors with the same contents as their device counterparts.
-    """
-    desc = cache_desc(k_cache, v_cache)
+def _attention_args(out, q, k_cache, block_tables, context_lens, query_start_loc,
+                    context_lens_host, query_start_loc_host):
     tq, hq, d = q.shape
     if tuple(out.shape) != (tq, hq, d) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
         raise ValueError("q/out must be [T_q][H_q][D] in the pool dtype")
@@ -215,12 +212,55 @@ def pa_attention(out, q, k_cache, v_cache, block_tables, context_lens, query_sta
             raise ValueError("host mirrors must be contiguous int32 CPU tensors")
     if block_tables.dim() != 2 or block_tables.shape[0] != s or query_start_loc.shape[0] != s + 1:
         raise ValueError("block_tables [S][max_blocks] and query_start_loc [S+1] expected")
+    return tq, hq, s
+
+
+def pa_attention(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                 context_lens_host, query_start_loc_host, scale: float, workspace,
+                 opt: PaOptions | None = None, stream=None) -> None:
+    """Causal paged attention of a ragged batch; writes ``out`` in place.
+
+    ``context_lens_host`` / ``query_start_loc_host`` are contiguous int32 CPU
+    tensors with the same contents as their device counterparts.
+    """
+    desc = cache_desc(k_cache, v_cache)
+    tq, hq, s = _attention_args(out, q, k_cache, block_tables, context_lens, query_start_loc,
+                                context_lens_host, query_start_loc_host)
     _check(LIB.pa_attention(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
                             hq, _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
                             _ptr(query_start_loc), s, tq, _ptr(context_lens_host),
                             _ptr(query_start_loc_host), float(scale), _ptr(workspace),
                             0 if workspace is None else int(workspace.numel() * workspace.element_size()),
                             ctypes.byref(opt) if opt is not None else None, _stream(stream)))
+
+
+def pa_write_kv_attention(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                          context_lens, query_start_loc, context_lens_host, query_start_loc_host,
+                          scale: float, workspace, opt: PaOptions | None = None,
+                          stream=None) -> None:
+    """``pa_write_kv`` of the batch's new tokens (row t of ``k_new`` /
+    ``v_new`` is query row t's token, stored at ``slot_mapping[t]``) followed
+    by ``pa_attention``, in one call (the write shares the planner's
+    launch)."""
+    desc = cache_desc(k_cache, v_cache)
+    tq, hq, s = _attention_args(out, q, k_cache, block_tables, context_lens, query_start_loc,
+                                context_lens_host, query_start_loc_host)
+    if tuple(k_new.shape) != (tq, desc.num_kv_heads, desc.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [T_q][H_kv][D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("k_new/v_new must have the pool dtype")
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new/v_new must be contiguous")
+    if (slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous()
+            or slot_mapping.numel() != tq):
+        raise ValueError("slot_mapping must be a contiguous int64 [T_q] tensor")
+    _check(LIB.pa_write_kv_attention(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
+        _ptr(v_cache), ctypes.byref(desc), hq, _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(context_lens), _ptr(query_start_loc), s, tq, _ptr(context_lens_host),
+        _ptr(query_start_loc_host), float(scale), _ptr(workspace),
+        0 if workspace is None else int(workspace.numel() * workspace.element_size()),
+        ctypes.byref(opt) if opt is not None else None, _stream(stream)))
 
 
 def version() -> int:

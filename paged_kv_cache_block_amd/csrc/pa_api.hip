@@ -128,6 +128,39 @@ WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q
   return w;
 }
 
+// PA_VALIDATE checks of a slot mapping: every slot inside the pool, no slot
+// twice.  The mapping is left in `slots`.
+pa_status check_slots(std::vector<int64_t>& slots, const int64_t* slot_mapping, int num_tokens,
+                      const PoolArgs& p, hipStream_t stream) {
+  pa_status st = fetch(slots, slot_mapping, (size_t)num_tokens, stream);
+  if (st != PA_OK) return st;
+  const int64_t total = (int64_t)p.num_blocks * p.block_size;
+  std::vector<int64_t> seen;
+  for (int64_t sl : slots) {
+    if (sl >= total) return fail(PA_ERR_BOUNDS, "slot %lld out of range", (long long)sl);
+    if (sl >= 0) seen.push_back(sl);
+  }
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+    return fail(PA_ERR_BOUNDS, "duplicate slot in slot_mapping");
+  return PA_OK;
+}
+
+// New tokens written by the fused entry point (null: plain attention).
+struct FusedWrite {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slots;
+};
+
+pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
+                         const pa_cache_desc* c, int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
+                         const int32_t* context_lens_host, const int32_t* query_start_loc_host,
+                         float scale, void* workspace, size_t workspace_bytes,
+                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -150,16 +183,7 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_
     return fail(PA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
   if (validate_mode()) {
     std::vector<int64_t> slots;
-    if ((st = fetch(slots, slot_mapping, (size_t)num_tokens, stream)) != PA_OK) return st;
-    const int64_t total = (int64_t)p.num_blocks * p.block_size;
-    std::vector<int64_t> seen;
-    for (int64_t sl : slots) {
-      if (sl >= total) return fail(PA_ERR_BOUNDS, "slot %lld out of range", (long long)sl);
-      if (sl >= 0) seen.push_back(sl);
-    }
-    std::sort(seen.begin(), seen.end());
-    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
-      return fail(PA_ERR_BOUNDS, "duplicate slot in slot_mapping");
+    if ((st = check_slots(slots, slot_mapping, num_tokens, p, stream)) != PA_OK) return st;
   }
   hipError_t e = launch_write_kv(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, p, stream);
   return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");
@@ -323,6 +347,41 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
                        const int32_t* context_lens_host, const int32_t* query_start_loc_host,
                        float scale, void* workspace, size_t workspace_bytes,
                        const pa_options* opt, hipStream_t stream) {
+  return attention_impl(out, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), c,
+                        num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                        query_start_loc, num_seqs, total_q, context_lens_host,
+                        query_start_loc_host, scale, workspace, workspace_bytes, opt, nullptr,
+                        stream);
+}
+
+pa_status pa_write_kv_attention(void* out, const void* q, const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                const pa_cache_desc* c, int32_t num_q_heads,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t total_q,
+                                const int32_t* context_lens_host,
+                                const int32_t* query_start_loc_host, float scale,
+                                void* workspace, size_t workspace_bytes, const pa_options* opt,
+                                hipStream_t stream) {
+  const FusedWrite fw{k_new, v_new, slot_mapping};
+  return attention_impl(out, q, k_cache, v_cache, c, num_q_heads, block_tables,
+                        max_blocks_per_seq, context_lens, query_start_loc, num_seqs, total_q,
+                        context_lens_host, query_start_loc_host, scale, workspace,
+                        workspace_bytes, opt, &fw, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
+                         const pa_cache_desc* c, int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
+                         const int32_t* context_lens_host, const int32_t* query_start_loc_host,
+                         float scale, void* workspace, size_t workspace_bytes,
+                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream) {
   PoolArgs p;
   pa_status st = check_desc(c, &p);
   if (st != PA_OK) return st;
@@ -368,6 +427,10 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_INVALID_ARG, "q, out and the pools must be 16-byte aligned");
+  if (fw && (!fw->k_new || !fw->v_new || !fw->slots))
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (fw && (!aligned16(fw->k_new) || !aligned16(fw->v_new)))
+    return fail(PA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
 
   const WorkspaceLayout lay = make_layout(p, num_q_heads, num_seqs, total_q, max_len, opt);
   if (!workspace || workspace_bytes < lay.total)
@@ -389,6 +452,10 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
         if (b < 0 || b >= p.num_blocks)
           return fail(PA_ERR_BOUNDS, "block_tables[%d][%d] = %d out of range", s, j, b);
       }
+    }
+    if (fw) {
+      std::vector<int64_t> slots;   // the pa_write_kv rules for the fused write
+      if ((st = check_slots(slots, fw->slots, total_q, p, stream)) != PA_OK) return st;
     }
   }
 
@@ -441,9 +508,14 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   if (n_rows > 0 && !rows_on_mfma && p.block_size > 64)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d needs the fp16/bf16 MFMA kernels", p.block_size);
 
+  // The plan, and with the fused write the new tokens' K/V stores too, in one
+  // launch ahead of every kernel that reads the pools.
   PlanParams pp{num_seqs, split, group, va ? 1 : 0, tile_rows, psplit,
                 lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials};
-  hipError_t e = launch_plan(context_lens, query_start_loc, pp, workspace, lay, stream);
+  hipError_t e =
+      fw ? launch_plan_write(context_lens, query_start_loc, pp, workspace, lay, fw->k_new,
+                             fw->v_new, fw->slots, total_q, k_cache, v_cache, p, stream)
+         : launch_plan(context_lens, query_start_loc, pp, workspace, lay, stream);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
 
   AttnArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
@@ -477,4 +549,4 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
   return PA_OK;
 }
 
-}  // extern "C"
+}  // namespace

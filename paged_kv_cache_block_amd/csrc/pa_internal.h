@@ -73,6 +73,12 @@ hipError_t launch_swap_kernel(const void* src_k, const void* src_v, void* dst_k,
                               const PoolArgs& p, const SwapPairs& pairs, int n, hipStream_t s);
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* qsl, const PlanParams& pp,
                        void* ws, const WorkspaceLayout& lay, hipStream_t s);
+// The plan and the slot-mapping write of num_tokens new tokens in one launch
+// (the plan reads no pool, the write no plan).
+hipError_t launch_plan_write(const int32_t* context_lens, const int32_t* qsl, const PlanParams& pp,
+                             void* ws, const WorkspaceLayout& lay, const void* k_new,
+                             const void* v_new, const int64_t* slots, int num_tokens,
+                             void* k_cache, void* v_cache, const PoolArgs& p, hipStream_t s);
 
 struct AttnArgs {
   void* out;

@@ -12,64 +12,19 @@
 // elements of consecutive slots are stored side by side.  Block copies move
 // 16-byte chunks.
 
-#include "pa_internal.h"
+#include "pa_write.h"
 
 namespace pa {
 namespace {
 
-// One launch, two kinds of workgroup, each with the thread order that makes
-// its stores contiguous.  The first k_blocks workgroups copy K: one thread per
-// 16-byte chunk of a (token, head) row, which stays a contiguous row of the
-// token-major block.  The rest write V with the token index fastest: thread
-// (head, chunk, token) loads the token's 16-byte chunk of head-dim elements
-// and stores each element into its head-dim row of the head-dim-major block,
-// so that, for consecutive slots, the lanes of a wave fill consecutive
-// positions of the same row.
 template <int EB>
 __global__ __launch_bounds__(256) void write_kv_kernel(
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
     const int64_t* __restrict__ slots, int64_t num_tokens, int64_t chunks, int k_blocks,
     int chunks_per_row, int H, int D, int bs, int64_t total_slots, uint8_t* __restrict__ k_cache,
     void* __restrict__ v_cache) {
-  using E = typename Elt<EB == 4 ? DT_F32 : DT_F16>::store_t;
-  constexpr int VEC = 16 / EB;
-  const bool is_k = (int)blockIdx.x < k_blocks;
-  const int64_t gid = (int64_t)(is_k ? blockIdx.x : blockIdx.x - k_blocks) * 256 + threadIdx.x;
-  if (gid >= chunks) return;
-  if (is_k) {
-    const int chunk = (int)(gid % chunks_per_row);
-    const int64_t th = gid / chunks_per_row;
-    const int h = (int)(th % H);
-    const int64_t t = th / H;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= total_slots) return;
-    const int64_t blk = slot / bs;
-    const int off = (int)(slot - blk * bs);
-    uint8_t* kdst = k_cache + (((blk * H + h) * bs + off) * (int64_t)D) * EB + (int64_t)chunk * 16;
-    *reinterpret_cast<uint4*>(kdst) = k_new[gid];
-    return;
-  }
-  const int64_t t = gid % num_tokens;
-  const int64_t hc = gid / num_tokens;
-  const int chunk = (int)(hc % chunks_per_row);
-  const int h = (int)(hc / chunks_per_row);
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= total_slots) return;
-  const int64_t blk = slot / bs;
-  const int off = (int)(slot - blk * bs);
-  const uint4 vv = v_new[(t * H + h) * chunks_per_row + chunk];
-  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-  E* vdst = reinterpret_cast<E*>(v_cache) + ((blk * H + h) * (int64_t)D + (int64_t)chunk * VEC) * bs + off;
-  if constexpr (EB == 4) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vdst[(int64_t)e * bs] = w[e];
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vdst[(int64_t)(2 * e) * bs] = (E)(w[e] & 0xffffu);
-      vdst[(int64_t)(2 * e + 1) * bs] = (E)(w[e] >> 16);
-    }
-  }
+  write_kv_block<EB>((int)blockIdx.x, k_new, v_new, slots, num_tokens, chunks, k_blocks,
+                     chunks_per_row, H, D, bs, total_slots, k_cache, v_cache);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
@@ -176,14 +131,12 @@ hipError_t launch_copy_blocks_layers(const LayerPools& lp, int num_layers, const
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int64_t* slots,
                            int num_tokens, void* k_cache, void* v_cache, const PoolArgs& p,
                            hipStream_t s) {
-  const int eb = p.dtype == DT_F32 ? 4 : 2;
-  const int cpr = p.head_dim * eb / 16;
-  const int64_t chunks = (int64_t)num_tokens * p.num_kv_heads * cpr;
+  const WriteGeom wg = write_geom(num_tokens, p);
+  const int eb = wg.eb, cpr = wg.cpr;
+  const int64_t chunks = wg.chunks, blocks = wg.blocks, total_slots = wg.total_slots;
   if (chunks == 0) return hipSuccess;
-  const int64_t blocks = (chunks + 255) / 256;     // for K, and again for V
   if (2 * blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(2 * blocks));
-  const int64_t total_slots = (int64_t)p.num_blocks * p.block_size;
   if (eb == 4)
     hipLaunchKernelGGL(write_kv_kernel<4>, grid, dim3(256), 0, s, (const uint4*)k_new,
                        (const uint4*)v_new, slots, (int64_t)num_tokens, chunks, (int)blocks, cpr,

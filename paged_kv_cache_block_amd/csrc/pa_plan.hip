@@ -6,8 +6,10 @@
 // query_start_loc into flat work lists inside the caller's workspace, so the
 // attention kernels launch compact grids and read one record each; the host
 // derives the same list sizes from the host mirrors to size those grids.
+// With the fused write (pa_write_kv_attention), the same launch also carries
+// the slot-mapping write: the plan reads no pool and the write no plan.
 
-#include "pa_internal.h"
+#include "pa_write.h"
 
 namespace pa {
 namespace {
@@ -19,10 +21,9 @@ struct SplitSeq {
   int32_t seq, comb_base, pbase, i0, n, L, q0, ns;
 };
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens,
-                                                           const int32_t* __restrict__ qsl,
-                                                           PlanParams pp, uint8_t* ws,
-                                                           WorkspaceLayout lay) {
+__device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
+                                           const int32_t* __restrict__ qsl, const PlanParams& pp,
+                                           uint8_t* ws, const WorkspaceLayout& lay) {
   __shared__ int32_t scan[4][kPlanThreads];
   __shared__ SplitSeq split_list[kSplitList];
   __shared__ int32_t split_count;
@@ -138,7 +139,57 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens,
+                                                           const int32_t* __restrict__ qsl,
+                                                           PlanParams pp, uint8_t* ws,
+                                                           WorkspaceLayout lay) {
+  plan_block(lens, qsl, pp, ws, lay);
+}
+
+// Workgroup 0 plans; the others write the new tokens' K/V.
+struct WriteArgs {
+  const uint4* k_new;
+  const uint4* v_new;
+  const int64_t* slots;
+  int64_t num_tokens, chunks, total_slots;
+  int k_blocks, cpr, H, D, bs;
+  uint8_t* k_cache;
+  void* v_cache;
+};
+template <int EB>
+__global__ __launch_bounds__(kPlanThreads) void plan_write_kernel(const int32_t* __restrict__ lens,
+                                                                 const int32_t* __restrict__ qsl,
+                                                                 PlanParams pp, uint8_t* ws,
+                                                                 WorkspaceLayout lay, WriteArgs w) {
+  static_assert(kPlanThreads == 256, "the write runs 256-thread workgroups");
+  if (blockIdx.x == 0) {
+    plan_block(lens, qsl, pp, ws, lay);
+    return;
+  }
+  write_kv_block<EB>((int)blockIdx.x - 1, w.k_new, w.v_new, w.slots, w.num_tokens, w.chunks,
+                     w.k_blocks, w.cpr, w.H, w.D, w.bs, w.total_slots, w.k_cache, w.v_cache);
+}
+
 }  // namespace
+
+hipError_t launch_plan_write(const int32_t* context_lens, const int32_t* qsl, const PlanParams& pp,
+                             void* ws, const WorkspaceLayout& lay, const void* k_new,
+                             const void* v_new, const int64_t* slots, int num_tokens,
+                             void* k_cache, void* v_cache, const PoolArgs& p, hipStream_t s) {
+  const WriteGeom g = write_geom(num_tokens, p);
+  if (1 + 2 * g.blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const WriteArgs w{(const uint4*)k_new, (const uint4*)v_new, slots, (int64_t)num_tokens, g.chunks,
+                    g.total_slots, (int)g.blocks, g.cpr, p.num_kv_heads, p.head_dim, p.block_size,
+                    (uint8_t*)k_cache, v_cache};
+  const dim3 grid((unsigned)(1 + 2 * g.blocks));
+  if (g.eb == 4)
+    hipLaunchKernelGGL(plan_write_kernel<4>, grid, dim3(kPlanThreads), 0, s, context_lens, qsl, pp,
+                       (uint8_t*)ws, lay, w);
+  else
+    hipLaunchKernelGGL(plan_write_kernel<2>, grid, dim3(kPlanThreads), 0, s, context_lens, qsl, pp,
+                       (uint8_t*)ws, lay, w);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const int32_t* context_lens, const int32_t* qsl, const PlanParams& pp,
                        void* ws, const WorkspaceLayout& lay, hipStream_t s) {

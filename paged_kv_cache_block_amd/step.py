@@ -1,8 +1,8 @@
 """Device-resident batch and one step of the hot path.
 
 A step is: copy-on-write block copies, the slot-mapping write of the new
-tokens' K/V, then causal paged attention of every query row -- the order the
-pages give (vLLM blog page, section 2.1: the copy happens before the write;
+tokens' K/V, then causal paged attention of every query row (the last two as
+one call when ``fused``) -- the order the pages give (vLLM blog page, section 2.1: the copy happens before the write;
 Pensieve page, 统一Prefill和Generation阶段的执行过程: K/V are stored before
 attention).
 
@@ -99,8 +99,21 @@ class DeviceBatch:
                              self.qsl_host, self.w.scale, self.workspace, opt)
         return out
 
-    def step(self) -> torch.Tensor:
+    def write_attention(self, out=None, opt="default") -> torch.Tensor:
+        """The new-token write and attention in one call (pa_write_kv_attention)."""
+        out = self.out if out is None else out
+        opt = self.opt if opt == "default" else opt
+        binding.pa_write_kv_attention(out, self.q, self.k_new, self.v_new, self.slot_mapping,
+                                      self.k_cache, self.v_cache, self.block_tables,
+                                      self.context_lens, self.query_start_loc,
+                                      self.context_lens_host, self.qsl_host, self.w.scale,
+                                      self.workspace, opt)
+        return out
+
+    def step(self, fused: bool = False) -> torch.Tensor:
         self.copy_blocks()
+        if fused:
+            return self.write_attention()
         self.write_new()
         return self.attention()
 

@@ -104,6 +104,37 @@ def test_attention_argument_errors(binding, case, expect):
     assert b.LIB.pa_last_error()
 
 
+@pytest.mark.parametrize("case,expect", [("null_k_new", -1), ("null_slots", -1),
+                                         ("misaligned_v_new", -1), ("n_gt_L", -1),
+                                         ("workspace", -3)])
+def test_write_attention_argument_errors(binding, case, expect):
+    """The fused entry point checks its write arguments with the attention
+    ones, on the host, before anything is enqueued."""
+    b = binding
+    desc = _desc(b)
+    lens, qsl, ws = [8, 5], [0, 1, 6], 1 << 20
+    fake = 1 << 20
+    k_new, v_new, slots = fake, fake, fake
+    if case == "null_k_new":
+        k_new = None
+    elif case == "null_slots":
+        slots = None
+    elif case == "misaligned_v_new":
+        v_new = fake + 4
+    elif case == "n_gt_L":
+        lens = [8, 4]
+    elif case == "workspace":
+        ws = 10
+    S = len(lens)
+    lh = (ctypes.c_int32 * S)(*lens)
+    qh = (ctypes.c_int32 * (S + 1))(*qsl)
+    st = b.LIB.pa_write_kv_attention(fake, fake, k_new, v_new, slots, fake, fake,
+                                     ctypes.byref(desc), 4, fake, 8, fake, fake, S, qsl[-1], lh,
+                                     qh, 0.125, fake, ws, None, None)
+    assert st == expect, (case, st, b.LIB.pa_last_error())
+    assert b.LIB.pa_last_error()
+
+
 def test_write_and_copy_argument_errors(binding):
     b = binding
     desc = _desc(b)

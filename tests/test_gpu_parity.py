@@ -61,12 +61,12 @@ def compare(got_storage, want64, dtype, rows=None, what=""):
     assert mean <= tmean, f"{what}: mean |d| {mean} > {tmean}"
 
 
-def run_gpu(w, opt=None, write_history=True):
+def run_gpu(w, opt=None, write_history=True, fused=False):
     torch = pytest.importorskip("torch")
     db = _step_mod().DeviceBatch(w, opt=opt)
     if write_history:
         db.write_history()
-    db.step()
+    db.step(fused=fused)
     torch.cuda.synchronize()
     return db
 
@@ -316,6 +316,69 @@ def test_shape_sweep(torch_cuda, shape):
         compare(db.out_numpy(), want, w.dtype, what=f"shape {shape} tile rows {rows}")
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("split", [0, 64])
+def test_fused_write_is_bit_identical(torch_cuda, cfg, split):
+    """pa_write_kv_attention gives the outputs and pools of pa_write_kv
+    followed by pa_attention, bit for bit, on every config (fp32, decode-only,
+    mixed).  Unwritten slots hold NaN, so a new token read before it is
+    stored would show."""
+    from paged_kv_cache_block_amd import binding
+    w = small_workload(cfg)
+    opt = binding.options(split) if split else None
+    say("fused write", w.name, "split", split)
+    a = run_gpu(w, opt)
+    b = run_gpu(w, opt, fused=True)
+    assert np.array_equal(bits(a.out_numpy()), bits(b.out_numpy()))
+    ka, va = a.pools_numpy()
+    kb, vb = b.pools_numpy()
+    assert np.array_equal(bits(ka), bits(kb))
+    assert np.array_equal(bits(va), bits(vb))
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    compare(b.out_numpy(), want, w.dtype, what=f"{w.name} fused write")
+
+
+@pytest.mark.parametrize("dtype,bs", [("f16", 16), ("bf16", 32), ("bf16", 64)])
+@pytest.mark.parametrize("split", [0, 64])
+def test_fused_write_step_aligned_contexts(torch_cuda, dtype, bs, split):
+    """Decode rows whose own token ends a 32-key step (contexts 32, 64, 96,
+    160), or starts one, or is alone, over three block sizes: the fused call
+    stores every new token before any attention kernel reads it."""
+    from paged_kv_cache_block_amd import binding
+    seqs = [(31, 1, 1), (63, 1, 1), (95, 1, 1), (159, 1, 1), (32, 1, 1), (0, 1, 1),
+            (64, 1, 1), (30, 1, 1)]
+    w = build_batch(f"aligned decodes {dtype} bs {bs}", dtype, 16, 4, 128, bs, 256, seqs, 5)
+    opt = binding.options(split) if split else None
+    say("fused aligned", dtype, bs, "split", split)
+    a = run_gpu(w, opt)
+    b = run_gpu(w, opt, fused=True)
+    assert np.array_equal(bits(a.out_numpy()), bits(b.out_numpy()))
+    ka, va = a.pools_numpy()
+    kb, vb = b.pools_numpy()
+    assert np.array_equal(bits(ka), bits(kb))
+    assert np.array_equal(bits(va), bits(vb))
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    compare(b.out_numpy(), want, w.dtype, what=f"aligned decodes {dtype} bs {bs} fused")
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_fused_write_full_size(torch_cuda, cfg):
+    """Full-size decode batches: fused and separate calls agree bit for bit."""
+    w = config_workload(cfg)
+    say("fused write full", w.name)
+    a = run_gpu(w)
+    b = run_gpu(w, fused=True)
+    assert np.array_equal(bits(a.out_numpy()), bits(b.out_numpy()))
+    ka, va = a.pools_numpy()
+    kb, vb = b.pools_numpy()
+    assert np.array_equal(bits(ka), bits(kb))
+    assert np.array_equal(bits(va), bits(vb))
+
+
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_streaming_hint_is_bit_identical(torch_cuda, cfg):
     """The no-sharing hint only changes the cache policy of the loads."""
@@ -420,6 +483,13 @@ def test_empty_and_error_paths(torch_cuda, monkeypatch):
     dup[1] = dup[0]
     with pytest.raises(binding.PagedAttnError) as ei:
         binding.pa_write_kv(db.k_new, db.v_new, dup, db.k_cache, db.v_cache)
+    assert ei.value.status == -5
+    say("validate: fused write with a duplicate slot")
+    with pytest.raises(binding.PagedAttnError) as ei:
+        binding.pa_write_kv_attention(db.out, db.q, db.k_new, db.v_new, dup, db.k_cache,
+                                      db.v_cache, db.block_tables, db.context_lens,
+                                      db.query_start_loc, db.context_lens_host, db.qsl_host,
+                                      w.scale, db.workspace)
     assert ei.value.status == -5
     monkeypatch.delenv("PA_VALIDATE")
     say("workspace too small")
