@@ -1,0 +1,299 @@
+// Hardware ceilings the attention kernels are measured against (MI355X,
+// gfx950).  A standalone program, built next to the library:
+//
+//   paged_kv_cache_block_amd/hw_probes read   HBM read rate: sequential and
+//                                             random 4 KB chunks, and the two
+//                                             load shapes the decode kernel
+//                                             could use for its K operand
+//   paged_kv_cache_block_amd/hw_probes lds    ds_read_b128 bytes per clock per CU
+//   paged_kv_cache_block_amd/hw_probes mfma   32x32x16 bf16 MFMA rate, and how
+//                                             vector work overlaps it within one
+//                                             wave and across two waves of a SIMD
+//
+// Every kernel writes one output element per thread into a buffer sized for
+// its grid and reads only inside its own input buffer.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define CK(x)                                                                         \
+  do {                                                                                \
+    hipError_t e_ = (x);                                                              \
+    if (e_ != hipSuccess) {                                                           \
+      fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      return 1;                                                                       \
+    }                                                                                 \
+  } while (0)
+
+namespace {
+
+constexpr double kNominalHz = 2.4e9;   // clock the published peaks assume
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// ---- read ------------------------------------------------------------------
+// Sequential: grid-stride over n 16-byte chunks, U loads in flight per thread.
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void read_seq(const u32x4* __restrict__ p, size_t n, uint32_t* out) {
+  const size_t stride = (size_t)gridDim.x * 256 * U;
+  u32x4 acc = {0, 0, 0, 0};
+  for (size_t i = (size_t)blockIdx.x * 256 * U + threadIdx.x; i + 256 * (U - 1) < n; i += stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(p + i + 256 * u) : p[i + 256 * u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Random 4 KB chunks (chunk-aligned, hashed from wave and iteration), 8 KB per
+// iteration per wave (8 loads of 1 KB in flight).  SHAPE 0: each load reads
+// 1 KB contiguously (lane = 16-byte chunk); SHAPE 1: each load reads 16 rows
+// of 64 bytes, rows 256 bytes apart (lane (row r, group c) = 16 bytes at
+// r * 256 + 64 * load + 16 * c), the shape of a 16x16x32 MFMA A operand over
+// 256-byte key rows.
+template <int SHAPE, bool NT>
+__global__ __launch_bounds__(64) void read_chunks(const u32x4* __restrict__ p, uint32_t nchunks,
+                                                  int iters, uint32_t* out) {
+  const int lane = threadIdx.x;
+  const int r = lane & 15, c = lane >> 4;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t ch = mix32(blockIdx.x * 7919u + it * 104729u + k * 31u) % nchunks;
+      const u32x4* base = p + (size_t)ch * 256;   // 4 KB = 256 chunks of 16 bytes
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const int idx = SHAPE == 0 ? l * 64 + lane : r * 16 + l * 4 + c;
+        v[k * 4 + l] = NT ? __builtin_nontemporal_load(base + idx) : base[idx];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  out[blockIdx.x * 64 + lane] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// ---- lds -------------------------------------------------------------------
+// Each wave reads 1 KB per ds_read_b128 (lane l: 16 bytes at l * 16 + 1 KB * j,
+// conflict free) from a 64 KB buffer.
+__global__ __launch_bounds__(512) void lds_read(uint32_t* out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[16384];
+  for (int i = threadIdx.x; i < 16384; i += 512) buf[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int off = ((lane * 4) + 256 * ((j + wv * 3 + it) & 63)) & 16383;
+      acc ^= *reinterpret_cast<const u32x4*>(&buf[off]);
+    }
+  }
+  out[blockIdx.x * 512 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// ---- mfma ------------------------------------------------------------------
+__device__ __forceinline__ void mfma_operands(u32x4& a, u32x4& b) {
+  const uint32_t lane = threadIdx.x & 63;
+  a = u32x4{lane * 3u, lane * 5u, lane * 7u, lane * 11u} & 0x3f003f00u;   // small bf16 values
+  b = u32x4{lane * 13u, lane * 17u, lane * 19u, lane * 23u} & 0x3f003f00u;
+}
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One wave: a dependent MFMA chain, each MFMA followed by NV independent
+// vector ops (fma, or exp2 when EXP), fenced so the order holds.
+template <int NV, bool EXP>
+__global__ __launch_bounds__(256) void mfma_then_valu(float* out, int iters) {
+  u32x4 a, b;
+  mfma_operands(a, b);
+  f32x16 c0 = {};
+  float x[16];
+  for (int i = 0; i < 16; ++i) x[i] = 0.001f * (threadIdx.x + i);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c0 = mfma(a, b, c0);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        if constexpr (EXP) x[v & 15] = __builtin_amdgcn_exp2f(x[v & 15]);
+        else x[v & 15] = fmaf(x[v & 15], 0.999f, 0.001f);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float s = 0.f;
+  for (int e = 0; e < 16; ++e) s += c0[e] + x[e];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+// 512-thread workgroups (two waves per SIMD; waves w and w + 4 share a SIMD):
+// waves 0-3 run a dependent MFMA chain (it_mfma x 4 MFMAs), waves 4-7 run 16
+// independent vector chains (it_valu x 16 ops; exp2 when EXP).
+template <bool EXP>
+__global__ __launch_bounds__(512) void mfma_and_valu_waves(float* out, int it_mfma, int it_valu) {
+  float s = 0.f;
+  if ((threadIdx.x >> 6) < 4) {
+    u32x4 a, b;
+    mfma_operands(a, b);
+    f32x16 c0 = {};
+    for (int it = 0; it < it_mfma; ++it) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c0 = mfma(a, b, c0);
+    }
+    for (int e = 0; e < 16; ++e) s += c0[e];
+  } else {
+    float x[16];
+    for (int i = 0; i < 16; ++i) x[i] = 0.001f * (threadIdx.x + i);
+    for (int it = 0; it < it_valu; ++it) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (EXP) x[i] = __builtin_amdgcn_exp2f(x[i]);
+        else x[i] = fmaf(x[i], 0.999f, 0.001f);
+      }
+    }
+    for (int i = 0; i < 16; ++i) s += x[i];
+  }
+  out[blockIdx.x * 512 + threadIdx.x] = s;
+}
+
+struct Timer {
+  hipEvent_t e0, e1;
+  Timer() {
+    (void)hipEventCreate(&e0);
+    (void)hipEventCreate(&e1);
+  }
+  ~Timer() {
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+  }
+  // Best of `reps` timed launches after one warm-up, in ms.
+  template <typename F>
+  float best(F launch, int reps = 5) {
+    launch();
+    (void)hipDeviceSynchronize();
+    float b = 1e30f;
+    for (int r = 0; r < reps; ++r) {
+      (void)hipEventRecord(e0);
+      launch();
+      (void)hipEventRecord(e1);
+      (void)hipEventSynchronize(e1);
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      if (ms < b) b = ms;
+    }
+    return b;
+  }
+};
+
+int probe_read(int cus) {
+  const size_t bytes = (size_t)4 << 30;
+  u32x4* p;
+  CK(hipMalloc(&p, bytes));
+  CK(hipMemset(p, 1, bytes));
+  const int max_grid = cus * 64;
+  uint32_t* out;
+  CK(hipMalloc(&out, sizeof(uint32_t) * 256 * (size_t)max_grid));
+  Timer t;
+  const size_t n = bytes / 16;
+  auto seq = [&](const char* name, void (*k)(const u32x4*, size_t, uint32_t*), int grid) {
+    const float ms = t.best([&] { hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, 0, p, n, out); });
+    printf("read sequential %-28s grid %6d : %.3f ms  %.2f TB/s\n", name, grid, ms, bytes / (ms * 1e-3) / 1e12);
+  };
+  for (int g : {cus * 8, cus * 32}) {
+    seq("16 B loads, 8 in flight", read_seq<8, false>, g);
+    seq("16 B nt loads, 8 in flight", read_seq<8, true>, g);
+  }
+  const int grid = cus * 32, iters = 64;   // grid * iters * 8 KB = 4 GiB read
+  const uint32_t nch = (uint32_t)(bytes / 4096);
+  auto chunks = [&](const char* name, void (*k)(const u32x4*, uint32_t, int, uint32_t*)) {
+    const float ms = t.best([&] { hipLaunchKernelGGL(k, dim3(grid), dim3(64), 0, 0, p, nch, iters, out); });
+    const double rb = (double)grid * iters * 8192;
+    printf("read random 4 KB chunks %-36s : %.3f ms  %.2f TB/s\n", name, ms, rb / (ms * 1e-3) / 1e12);
+  };
+  chunks("1 KB contiguous per load, nt", read_chunks<0, true>);
+  chunks("16 rows x 64 B per load, nt", read_chunks<1, true>);
+  chunks("1 KB contiguous per load", read_chunks<0, false>);
+  chunks("16 rows x 64 B per load", read_chunks<1, false>);
+  CK(hipFree(p));
+  CK(hipFree(out));
+  return 0;
+}
+
+int probe_lds(int cus) {
+  uint32_t* out;
+  CK(hipMalloc(&out, sizeof(uint32_t) * 512 * (size_t)cus * 2));
+  Timer t;
+  for (int wgs = 1; wgs <= 2; ++wgs) {
+    const int grid = cus * wgs, iters = 4096;
+    const float ms = t.best([&] { hipLaunchKernelGGL(lds_read, dim3(grid), dim3(512), 0, 0, out, iters); });
+    const double b = (double)grid * 8 * iters * 16 * 1024;
+    printf("lds ds_read_b128, %d workgroups of 8 waves per CU: %.3f ms, %.1f TB/s, %.1f B/clk/CU at 2.4 GHz\n",
+           wgs, ms, b / (ms * 1e-3) / 1e12, b / (ms * 1e-3) / cus / kNominalHz);
+  }
+  CK(hipFree(out));
+  return 0;
+}
+
+int probe_mfma(int cus) {
+  float* out;
+  CK(hipMalloc(&out, sizeof(float) * 512 * (size_t)cus));
+  Timer t;
+  const int iters = 20000;
+  auto one_wave = [&](const char* name, void (*k)(float*, int)) {
+    const float ms = t.best([&] { hipLaunchKernelGGL(k, dim3(cus), dim3(256), 0, 0, out, iters); });
+    printf("one wave per SIMD, MFMA chain %-22s : %.1f cycles per MFMA at 2.4 GHz (%.0f TFLOP/s)\n", name,
+           ms * 1e-3 * kNominalHz / (iters * 4.0), (double)cus * 4 * iters * 4 * 32768.0 / (ms * 1e-3) / 1e12);
+  };
+  one_wave("alone", mfma_then_valu<0, false>);
+  one_wave("+ 4 fma per MFMA", mfma_then_valu<4, false>);
+  one_wave("+ 8 fma per MFMA", mfma_then_valu<8, false>);
+  one_wave("+ 16 fma per MFMA", mfma_then_valu<16, false>);
+  one_wave("+ 2 exp2 per MFMA", mfma_then_valu<2, true>);
+  one_wave("+ 8 exp2 per MFMA", mfma_then_valu<8, true>);
+  auto two_waves = [&](const char* name, void (*k)(float*, int, int), int im, int iv) {
+    const float ms = t.best([&] { hipLaunchKernelGGL(k, dim3(cus), dim3(512), 0, 0, out, im, iv); });
+    printf("two waves per SIMD, %-44s : %.3f ms\n", name, ms);
+  };
+  two_waves("MFMA wave alone (40K MFMAs)", mfma_and_valu_waves<false>, 10000, 0);
+  two_waves("fma wave alone (160K fma)", mfma_and_valu_waves<false>, 0, 10000);
+  two_waves("exp2 wave alone (160K exp2)", mfma_and_valu_waves<true>, 0, 10000);
+  two_waves("MFMA wave beside fma wave", mfma_and_valu_waves<false>, 10000, 10000);
+  two_waves("MFMA wave beside exp2 wave", mfma_and_valu_waves<true>, 10000, 10000);
+  CK(hipFree(out));
+  return 0;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  const char* mode = argc > 1 ? argv[1] : "";
+  hipDeviceProp_t prop;
+  CK(hipGetDeviceProperties(&prop, 0));
+  printf("device %s, %d CUs, clock %d kHz\n", prop.name, prop.multiProcessorCount, prop.clockRate);
+  if (!strcmp(mode, "read")) return probe_read(prop.multiProcessorCount);
+  if (!strcmp(mode, "lds")) return probe_lds(prop.multiProcessorCount);
+  if (!strcmp(mode, "mfma")) return probe_mfma(prop.multiProcessorCount);
+  fprintf(stderr, "usage: %s read|lds|mfma\n", argv[0]);
+  return 2;
+}
