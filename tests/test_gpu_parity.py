@@ -379,6 +379,36 @@ def test_fused_write_full_size(torch_cuda, cfg):
     assert np.array_equal(bits(va), bits(vb))
 
 
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_graph_capture_replays(torch_cuda, cfg):
+    """The fused write + attention call (plan + write, multi-token and decode
+    kernels, split combine) captured in a HIP graph replays to the eager
+    result, three times, with eager calls and synchronizations between the
+    replays."""
+    torch = torch_cuda
+    w = small_workload(cfg)
+    say("graph capture", w.name)
+    db = _step_mod().DeviceBatch(w)
+    db.write_history()
+    db.copy_blocks()
+    db.write_attention()
+    torch.cuda.synchronize()
+    want = bits(db.out_numpy()).copy()
+    out_g = torch.empty_like(db.out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        db.write_attention(out=out_g)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out_g.zero_()
+        db.write_attention()          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = bits(db.out_numpy(out_g))
+        assert np.array_equal(got, want), f"replay {r}"
+
+
 @pytest.mark.parametrize("cfg", [2, 5])
 def test_streaming_hint_is_bit_identical(torch_cuda, cfg):
     """The no-sharing hint only changes the cache policy of the loads."""
