@@ -94,9 +94,10 @@ __global__ __launch_bounds__(64) void read_chunks(const u32x4* __restrict__ p, u
 // ---- lds -------------------------------------------------------------------
 // Each wave reads 1 KB per ds_read_b128 (lane l: 16 bytes at l * 16 + 1 KB * j,
 // conflict free) from a 64 KB buffer.
-__global__ __launch_bounds__(512) void lds_read(uint32_t* out, int iters) {
+template <int NT>
+__global__ __launch_bounds__(NT) void lds_read(uint32_t* out, int iters) {
   __shared__ __attribute__((aligned(16))) uint32_t buf[16384];
-  for (int i = threadIdx.x; i < 16384; i += 512) buf[i] = i * 2654435761u;
+  for (int i = threadIdx.x; i < 16384; i += NT) buf[i] = i * 2654435761u;
   __syncthreads();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   u32x4 acc = {0, 0, 0, 0};
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(512) void lds_read(uint32_t* out, int iters) {
       acc ^= *reinterpret_cast<const u32x4*>(&buf[off]);
     }
   }
-  out[blockIdx.x * 512 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  out[blockIdx.x * NT + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
 // ---- mfma ------------------------------------------------------------------
@@ -242,15 +243,23 @@ int probe_read(int cus) {
 
 int probe_lds(int cus) {
   uint32_t* out;
-  CK(hipMalloc(&out, sizeof(uint32_t) * 512 * (size_t)cus * 2));
+  CK(hipMalloc(&out, sizeof(uint32_t) * 1024 * (size_t)cus * 2));
   Timer t;
-  for (int wgs = 1; wgs <= 2; ++wgs) {
-    const int grid = cus * wgs, iters = 4096;
-    const float ms = t.best([&] { hipLaunchKernelGGL(lds_read, dim3(grid), dim3(512), 0, 0, out, iters); });
-    const double b = (double)grid * 8 * iters * 16 * 1024;
-    printf("lds ds_read_b128, %d workgroups of 8 waves per CU: %.3f ms, %.1f TB/s, %.1f B/clk/CU at 2.4 GHz\n",
-           wgs, ms, b / (ms * 1e-3) / 1e12, b / (ms * 1e-3) / cus / kNominalHz);
-  }
+  const int iters = 4096;
+  auto run = [&](void (*k)(uint32_t*, int), int waves, int wgs) {
+    const int grid = cus * wgs;
+    const float ms = t.best([&] { hipLaunchKernelGGL(k, dim3(grid), dim3(64 * waves), 0, 0, out, iters); });
+    const double b = (double)grid * waves * iters * 16 * 1024;
+    printf("lds ds_read_b128, %d workgroup(s) of %2d waves per CU (%2d waves/CU): %.3f ms, %.1f TB/s, "
+           "%.1f B/clk/CU at 2.4 GHz\n", wgs, waves, waves * wgs, ms, b / (ms * 1e-3) / 1e12,
+           b / (ms * 1e-3) / cus / kNominalHz);
+  };
+  run(lds_read<256>, 4, 1);
+  run(lds_read<256>, 4, 2);
+  run(lds_read<512>, 8, 1);
+  run(lds_read<512>, 8, 2);
+  run(lds_read<1024>, 16, 1);
+  run(lds_read<1024>, 16, 2);
   CK(hipFree(out));
   return 0;
 }
