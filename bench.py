@@ -45,6 +45,15 @@ def work_model(w):
     row_q = int(n[dec].sum()) * w.num_q_heads * w.head_dim * elt
     m = {}
     m["rows_bytes"] = int((L[dec] * kvb).sum()) + 2 * row_q       # KV once per KV head + q + out
+    # The same with each cached slot counted once however many decode rows
+    # read it (sequences sharing prompt blocks by reference count).
+    used = {}
+    for s in np.flatnonzero(dec):
+        nb = (int(L[s]) + w.block_size - 1) // w.block_size
+        for j in range(nb):
+            b = int(w.block_tables[s, j])
+            used[b] = max(used.get(b, 0), min(w.block_size, int(L[s]) - j * w.block_size))
+    m["rows_unique_bytes"] = sum(used.values()) * kvb + 2 * row_q
     m["tile_bytes"] = int((L[mt] * kvb).sum()) + 2 * int(n[mt].sum()) * w.num_q_heads * w.head_dim * elt
     m["tile_flops"] = int(4 * w.head_dim * w.num_q_heads *
                           (n[mt] * (L[mt] - n[mt]) + n[mt] * (n[mt] + 1) // 2).sum())
@@ -631,6 +640,10 @@ def main(argv=None) -> int:
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": rows_kernel, "algorithmic_bytes": model["rows_bytes"],
                 "avg_ms": round(dom_ms, 5)}
+        if model["rows_unique_bytes"] < model["rows_bytes"]:
+            # Blocks shared by several rows: the same rate over bytes counted once.
+            roof["unique_bytes"] = model["rows_unique_bytes"]
+            roof["achieved_unique"] = round(model["rows_unique_bytes"] / (dom_ms * 1e-3) / 1e9, 1)
     else:
         achieved = model["tile_flops"] / (dom_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[w.dtype]

@@ -6,7 +6,8 @@
 // bound by HBM (vLLM blog page, 挑战), so the design goal is that every byte of
 // K and V is read once per KV head and that enough of them are in flight.
 //
-// One wavefront owns one (sequence, KV head, key split).  The up-to-16 query
+// One wavefront owns one (sequence, KV head, key split); wavefronts are
+// numbered so that consecutive work items run on one XCD.  The up-to-16 query
 // heads of the KV head's group form the columns of 16x16 MFMA tiles, so a K/V
 // load serves all of them:
 //   S^T[key][head]  = K[key][:] . Q[head][:]      v_mfma_f32_16x16x32_{f16,bf16}
@@ -93,15 +94,21 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs
 
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
   const PlanCounts* pc = reinterpret_cast<const PlanCounts*>(ws + lay.counts);
-  if ((int)blockIdx.x >= pc->rows) return;
-  const RowItem it = reinterpret_cast<const RowItem*>(ws + lay.rows)[blockIdx.x];
+  // Work items (row splits) in plan order, each over all KV heads, numbered
+  // so that consecutive items -- the splits of one row, and rows of adjacent
+  // sequences, which share prompt blocks when a block manager forks them --
+  // run on one XCD.
+  const int Hkv = p.num_kv_heads;
+  const int logical = xcd_order(blockIdx.x, gridDim.x);
+  const int item = logical / Hkv;
+  const int g = logical - item * Hkv;
+  if (item >= pc->rows) return;
+  const RowItem it = reinterpret_cast<const RowItem*>(ws + lay.rows)[item];
 
   const int lane = threadIdx.x;
   const int c16 = lane & 15;       // MFMA row of A / column of B and C
   const int grp = lane >> 4;       // k-group of A and B; row group of C
-  const int g = blockIdx.y;
   const int Hq = a.num_q_heads;
-  const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int s = it.seq;
   const int q0 = a.qsl[s];
@@ -279,7 +286,8 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs
 template <int DT, int D, bool NT>
 hipError_t launch_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay, int items,
                     int split, hipStream_t s) {
-  const dim3 grid(items, p.num_kv_heads);
+  if ((int64_t)items * p.num_kv_heads > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(items * p.num_kv_heads);
   if (p.block_size == 16)
     hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 16, NT>), grid, dim3(64), 0, s, a, p, lay, split);
   else if (p.block_size == 32)

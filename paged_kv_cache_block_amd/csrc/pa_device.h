@@ -84,6 +84,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Logical work index of workgroup `bid` of an n-workgroup 1-D grid.  The
+// dispatcher hands workgroups to the 8 XCDs round-robin; this numbering gives
+// each XCD one contiguous range of logical indices, so work items that read
+// the same K/V (consecutive logical indices) share that XCD's L2.
+__device__ __forceinline__ int xcd_order(int bid, int n) {
+  const int xcd = bid & 7, pos = bid >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return xcd * per + min(xcd, rem) + pos;
+}
+
 // x and its copy in lane l ^ M (M = 16 or 32), by v_permlane16_swap /
 // v_permlane32_swap: a VALU op, where a shuffle would be an LDS round trip.
 // Each lane receives its own value in one result and its partner's in the

@@ -89,15 +89,6 @@ __device__ __forceinline__ int row_key(int r) {
   return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
 }
 
-// Logical work index of this workgroup: consecutive logical indices share
-// K/V, and each XCD (workgroups dispatched round-robin over 8) gets one
-// contiguous range of them.
-__device__ __forceinline__ int xcd_order(int bid, int n) {
-  const int xcd = bid & 7, pos = bid >> 3;
-  const int per = n >> 3, rem = n & 7;
-  return xcd * per + min(xcd, rem) + pos;
-}
-
 // NW = waves per workgroup (4 or 8), 32 rows each: the K/V tile staged in
 // LDS serves 32 * NW rows, so larger workgroups issue fewer loads and LDS
 // stores per MFMA.  Two waves per SIMD either way.
