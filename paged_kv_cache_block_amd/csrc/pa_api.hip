@@ -68,10 +68,11 @@ pa_status fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
 
 // Split length of row work.  `total_keys` is the sum over rows of the keys
 // each row attends to (only known at call time; -1 in size queries).
-int choose_split(const pa_options* opt, int64_t total_keys, int num_kv_heads) {
+int choose_split(const pa_options* opt, int64_t total_keys, int num_kv_heads, int group) {
   if (opt && opt->decode_split_tokens > 0) return (opt->decode_split_tokens + 63) / 64 * 64;
   if (total_keys < 0) return kMinAutoSplit;
-  int64_t want = (total_keys * num_kv_heads + kAutoTargetWaves - 1) / kAutoTargetWaves;
+  const int64_t target = (int64_t)kAutoTargetWaves * 2 / (group + 1);
+  int64_t want = (total_keys * num_kv_heads + target - 1) / target;
   want = (want + 63) / 64 * 64;
   return (int)std::min<int64_t>(kMaxAutoSplit, std::max<int64_t>(kMinAutoSplit, want));
 }
@@ -96,7 +97,7 @@ WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q
   const int64_t row_rows = va ? total_q : std::min(num_seqs, total_q);
   const int group = hq / p.num_kv_heads;
   if (opt && opt->decode_split_tokens > 0) {
-    const int split = choose_split(opt, -1, p.num_kv_heads);
+    const int split = choose_split(opt, -1, p.num_kv_heads, group);
     w.cap_rows = row_rows * row_splits(std::max(max_len, 1), split);
   } else {
     // Every row has at most keys/split + 1 splits.  With the automatic split,
@@ -468,7 +469,7 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
     const SeqWork w = seq_work(n, va ? 1 : 0, group, kTileRows);
     for (int i = w.row_first; i < w.row_first + w.rows; ++i) total_keys += L - n + i + 1;
   }
-  const int split = choose_split(opt, total_keys, p.num_kv_heads);
+  const int split = choose_split(opt, total_keys, p.num_kv_heads, group);
   // Wide (256-row) multi-token work items when there are enough of them.
   int tile_rows = kTileRows;
   if (opt && opt->prefill_tile_rows) {

@@ -18,9 +18,11 @@ constexpr int kTileRowsWide = 256;
 // tile loads and LDS stores per MFMA; they pay off once a batch has enough of
 // them to keep every CU busy.
 constexpr int kWideTileMinGroups = 1024;
-// Automatic split length of single-row work: about kAutoTargetWaves
-// wavefronts over the whole batch, clamped to [kMinAutoSplit, kMaxAutoSplit]
-// keys and rounded to a multiple of 64.
+// Automatic split length of single-row work: about kAutoTargetWaves * 2 /
+// (G + 1) wavefronts over the whole batch (G query heads per KV head: every
+// split of a row writes G partial states for the combine, so larger groups
+// take fewer, longer splits), clamped to [kMinAutoSplit, kMaxAutoSplit] keys
+// and rounded to a multiple of 64.
 constexpr int kAutoTargetWaves = 8192;
 // Multi-token key splits are whole numbers of this many keys (the largest
 // MFMA tile), so no tile straddles two splits.
