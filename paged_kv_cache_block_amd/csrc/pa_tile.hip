@@ -98,16 +98,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   constexpr int NT = 64 * NW;       // threads per workgroup
   constexpr int KS = D / 16;        // k-steps of the QK product
   constexpr int NDT = D / 32;       // 32-row head-dim tiles of O^T
-  constexpr int KROW = D + 8;       // LDS row stride of K (elements), padded
   // Keys per iteration: 128 for 8 waves (one register set of loads in
   // flight), 64 for 4 waves (two sets).
   constexpr int kKeys = NW == 8 ? 128 : 64;
   constexpr int NH = kKeys / 32;    // 32-key halves per tile
-  constexpr int VROW = kKeys + 8;   // LDS row stride of V^T (elements), padded
   constexpr int KCH = kKeys * D / 8 / NT;    // 16-byte K chunks per thread per tile
   constexpr int VCH = D * kKeys / 8 / NT;    // 16-byte V chunks per thread per tile
-  constexpr int KSTAGE = kKeys * KROW;
-  constexpr int VSTAGE = D * VROW;
+  // LDS holds each tile in MFMA operand order: one 16-byte slot per lane, a
+  // "run" of 32 slots per lane half, so that an operand read is two
+  // contiguous 512-byte runs (one base address per lane plus an immediate).
+  // Run r of K is (32-key half u, k-step ks, lane half hh) with
+  // r = 2 (u KS + ks) + hh; run r of V^T is (u, head-dim tile t, k-step v2,
+  // hh) with r = 4 (u NDT + t) + 2 v2 + hh.  The run pitch carries p extra
+  // slots, chosen so that the 16 lanes of each quarter-wave tile store hit 16
+  // distinct 16-byte bank groups: the 16 chunks of one key (p = 1) or two
+  // keys (p = 2) for K, and 4 head-dim rows x 4 key chunks for V (p = 4).
+  // Reads are 16 consecutive slots per quarter wave, conflict-free as well.
+  constexpr int KRUN = 8 * (32 + (D == 128 ? 1 : 2));   // K run pitch (elements)
+  constexpr int VRUN = 8 * (32 + 4);                    // V^T run pitch (elements)
+  constexpr int KSTAGE = 2 * NH * KS * KRUN;
+  constexpr int VSTAGE = 4 * NH * NDT * VRUN;
   constexpr int TROWS = 32 * NW;    // rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KSTAGE];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VSTAGE];
@@ -175,23 +185,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   float m_run = -INFINITY, l_run = 0.f;
 
   // Per-thread parts of the tile loads.  K chunk j is key kt0 + ktok + KRP*j,
-  // head-dim chunk kdc; V chunk j is head-dim row vd + 32*j, keys
-  // kt0 + vkey .. +8.  Offsets are within a block's (block, head) slice.
+  // head-dim chunk kdc.  V chunk j is head-dim row 4 (vdg + VDP j) + (tid>>2 & 3),
+  // keys kt0 + vkey .. +8 with vkey = 32 (vgrp % NH) + 8 (tid & 3): four lanes
+  // read 64 contiguous bytes of a row.  Offsets are within a block's
+  // (block, head) slice.
   constexpr int TPR = D / 8;            // 16-byte chunks per K row
   constexpr int KRP = NT / TPR;         // K rows per pass of the workgroup
-  constexpr int CPR = kKeys / 8;        // 16-byte chunks per V^T row of a tile
-  constexpr int VRP = NT / CPR;         // V^T rows per pass of the workgroup
+  constexpr int VDP = NT / 16 / NH;     // 4-row head-dim groups per pass
   const int ktok = tid / TPR;
   const int kdc = tid % TPR;
-  const int vd = tid / CPR;
-  const int vkey = 8 * (tid % CPR);
+  const int vgrp = tid >> 4;
+  const int vd = 4 * (vgrp / NH) + ((tid >> 2) & 3);
+  const int vkey = 32 * (vgrp % NH) + 8 * (tid & 3);
   const uint64_t kstride = (uint64_t)Hkv * BS * D;     // elements per physical block
   int kofs[KCH];
 #pragma unroll
   for (int j = 0; j < KCH; ++j) kofs[j] = ((g * BS + (ktok + KRP * j) % BS) * D) + kdc * 8;
   int vofs[VCH];
 #pragma unroll
-  for (int j = 0; j < VCH; ++j) vofs[j] = ((g * D + vd + VRP * j) * BS) + vkey % BS;
+  for (int j = 0; j < VCH; ++j) vofs[j] = ((g * D + vd + 4 * VDP * j) * BS) + vkey % BS;
 
   const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache);
@@ -247,34 +259,46 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
         }
     }
   };
+  // Operand-order slots of this thread's chunks (see KRUN / VRUN).  Key
+  // ktok + KRP j sits at a fixed offset from key ktok's slot: KRP is 16
+  // (then ktok < 16 and row_key adds 16 to it) or a multiple of 32; the
+  // head-dim rows of V chunk j step by 4 VDP = 32.
+  static_assert(KRP == 16 || KRP % 32 == 0, "K rows per pass");
+  static_assert(4 * VDP == 32, "V^T rows per pass");
+  const int kslot = (2 * KS * (ktok >> 5) + kdc) * KRUN + 8 * row_key(ktok & 31);
+  const int vslot = (4 * NDT * (vkey >> 5) + ((vkey >> 3) & 3) + 4 * (vd >> 5)) * VRUN + 8 * (vd & 31);
   auto store_tile = [&](const Buf& b, int stage) {
-    uint16_t* kd = Ks + stage * KSTAGE + ktok * KROW + kdc * 8;
-    uint16_t* vd_ = Vs + stage * VSTAGE + vd * VROW + vkey;
+    uint16_t* kd = Ks + stage * KSTAGE + kslot;
+    uint16_t* vd_ = Vs + stage * VSTAGE + vslot;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) *reinterpret_cast<u32x4*>(kd + KRP * j * KROW) = b.k[j];
+    for (int j = 0; j < KCH; ++j)
+      *reinterpret_cast<u32x4*>(kd + 2 * KS * KRUN * ((KRP * j) >> 5) + 8 * ((KRP * j) & 31)) = b.k[j];
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) *reinterpret_cast<u32x4*>(vd_ + VRP * j * VROW) = b.v[j];
+    for (int j = 0; j < VCH; ++j) *reinterpret_cast<u32x4*>(vd_ + 4 * VRUN * j) = b.v[j];
   };
 
   const int kt_first = k0 / kKeys;                 // splits are whole tiles
   const int kt_end = (k1 + kKeys - 1) / kKeys;
-  const int krow = row_key(col);
   const int wend = wave_on ? L - n + (min(R, wr0 + 32) - 1) / G + 1 : 0;
   // LDS operand reads of one 32-key half: K rows for S^T, V^T rows for O^T.
   // They are issued ahead of the MFMAs that consume them (the V^T of a half
   // and the K of the next half before the half's softmax), so their latency
   // hides behind that vector work.
+  // Lane (col, hh) of a K operand holds key 32u + row_key(col): the store
+  // put key 32u + k at slot row_key(k), and row_key is its own inverse.
+  const int klane = hh * KRUN + 8 * col;
+  const int vlane = hh * VRUN + 8 * col;
   auto read_k = [&](const uint16_t* ks_, int u, u32x4 (&kop)[KS]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      kop[ks] = *reinterpret_cast<const u32x4*>(&ks_[(32 * u + krow) * KROW + 16 * ks + 8 * hh]);
+      kop[ks] = *reinterpret_cast<const u32x4*>(&ks_[klane + 2 * (u * KS + ks) * KRUN]);
   };
   auto read_v = [&](const uint16_t* vs_, int u, u32x4 (&vop)[NDT][2]) {
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int v2 = 0; v2 < 2; ++v2)
-        vop[t][v2] = *reinterpret_cast<const u32x4*>(&vs_[(32 * t + col) * VROW + 32 * u + 16 * v2 + 8 * hh]);
+        vop[t][v2] = *reinterpret_cast<const u32x4*>(&vs_[vlane + (4 * (u * NDT + t) + 2 * v2) * VRUN]);
   };
   auto compute = [&](int kt, int stage) {
     const int kt0 = kt * kKeys;

@@ -6,6 +6,9 @@
 //                                             load shapes the decode kernel
 //                                             could use for its K operand
 //   paged_kv_cache_block_amd/hw_probes lds    ds_read_b128 bytes per clock per CU
+//   paged_kv_cache_block_amd/hw_probes ldsmap ds_read_b128 rate for the lane ->
+//                                             address maps an MFMA operand read
+//                                             from a padded or swizzled tile uses
 //   paged_kv_cache_block_amd/hw_probes mfma   32x32x16 bf16 MFMA rate, and how
 //                                             vector work overlaps it within one
 //                                             wave and across two waves of a SIMD
@@ -109,6 +112,57 @@ __global__ __launch_bounds__(NT) void lds_read(uint32_t* out, int iters) {
     }
   }
   out[blockIdx.x * NT + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// ---- ldsmap ----------------------------------------------------------------
+// Byte address read by lane `lane` for map M: a 64-lane ds_read_b128 of one
+// 32x32x16 MFMA operand, lane (c = lane & 31, h = lane >> 5) taking 16 bytes
+// of row r(c) at column chunk h of a tile with the given row pitch.
+//   0: contiguous 1 KB (lane * 16)
+//   1: r = c, pitch 272 B (128 16-bit values + 8 of padding)
+//   2: r = a permutation of c (16 (c>>4) + 8 ((c>>2)&1) + 4 ((c>>3)&1) + (c&3)), pitch 272 B
+//   3: r = c, pitch 256 B (no padding)
+//   4: r = c, pitch 256 B, 16-byte chunk index XOR (r & 15)
+//   5: r = c, pitch 264 B
+//   6: r = c, pitch 288 B
+//   7: permuted r as in 2, pitch 256 B, chunk XOR (r & 15)
+//   8: r = c, pitch 256 B, chunk XOR ((r >> 1) & 15)
+//   9: permuted r as in 2, pitch 288 B
+__device__ __forceinline__ uint32_t lds_map(int m, int lane) {
+  const int c = lane & 31, h = lane >> 5;
+  const int rp = 16 * (c >> 4) + 8 * ((c >> 2) & 1) + 4 * ((c >> 3) & 1) + (c & 3);
+  switch (m) {
+    case 0: return lane * 16;
+    case 1: return c * 272 + 16 * h;
+    case 2: return rp * 272 + 16 * h;
+    case 3: return c * 256 + 16 * h;
+    case 4: return c * 256 + 16 * (h ^ (c & 15));
+    case 5: return c * 264 + 16 * h;
+    case 6: return c * 288 + 16 * h;
+    case 7: return rp * 256 + 16 * (h ^ (rp & 15));
+    case 8: return c * 256 + 16 * (h ^ ((c >> 1) & 15));
+    default: return rp * 288 + 16 * h;
+  }
+}
+
+// 8 waves, each issuing 16 reads per iteration at lds_map(M) plus a per-read
+// offset that is a multiple of 4 KB (so the bank pattern is the map's).
+template <int M>
+__global__ __launch_bounds__(512) void lds_map_read(uint32_t* out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[16384];   // 64 KB
+  for (int i = threadIdx.x; i < 16384; i += 512) buf[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t a = lds_map(M, lane);   // < 32 * 288 = 9216
+  u32x4 acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t off = (4096u * ((j + wv * 3 + it) % 13) + a) / 4;   // < 49152 + 9216 bytes
+      acc ^= *reinterpret_cast<const u32x4*>(&buf[off]);
+    }
+  }
+  out[blockIdx.x * 512 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
 // ---- mfma ------------------------------------------------------------------
@@ -264,6 +318,31 @@ int probe_lds(int cus) {
   return 0;
 }
 
+int probe_ldsmap(int cus) {
+  uint32_t* out;
+  CK(hipMalloc(&out, sizeof(uint32_t) * 512 * (size_t)cus * 2));
+  Timer t;
+  const int iters = 4096;
+  const char* names[] = {"contiguous 1 KB", "rows, pitch 272 B", "permuted rows, pitch 272 B",
+                         "rows, pitch 256 B", "rows, pitch 256 B, chunk ^ (r & 15)", "rows, pitch 264 B",
+                         "rows, pitch 288 B", "permuted rows, pitch 256 B, chunk ^ (r & 15)",
+                         "rows, pitch 256 B, chunk ^ ((r >> 1) & 15)", "permuted rows, pitch 288 B"};
+  void (*kern[])(uint32_t*, int) = {lds_map_read<0>, lds_map_read<1>, lds_map_read<2>, lds_map_read<3>,
+                                    lds_map_read<4>, lds_map_read<5>, lds_map_read<6>, lds_map_read<7>,
+                                    lds_map_read<8>, lds_map_read<9>};
+  for (int m = 0; m < 10; ++m) {
+    for (int wgs : {1, 2}) {
+      const int grid = cus * wgs;
+      const float ms = t.best([&] { hipLaunchKernelGGL(kern[m], dim3(grid), dim3(512), 0, 0, out, iters); });
+      const double b = (double)grid * 8 * iters * 16 * 1024;
+      printf("ldsmap %-46s %2d waves/CU: %.1f B/clk/CU at 2.4 GHz\n", names[m], 8 * wgs,
+             b / (ms * 1e-3) / cus / kNominalHz);
+    }
+  }
+  CK(hipFree(out));
+  return 0;
+}
+
 int probe_mfma(int cus) {
   float* out;
   CK(hipMalloc(&out, sizeof(float) * 512 * (size_t)cus));
@@ -303,6 +382,7 @@ int main(int argc, char** argv) {
   if (!strcmp(mode, "read")) return probe_read(prop.multiProcessorCount);
   if (!strcmp(mode, "lds")) return probe_lds(prop.multiProcessorCount);
   if (!strcmp(mode, "mfma")) return probe_mfma(prop.multiProcessorCount);
-  fprintf(stderr, "usage: %s read|lds|mfma\n", argv[0]);
+  if (!strcmp(mode, "ldsmap")) return probe_ldsmap(prop.multiProcessorCount);
+  fprintf(stderr, "usage: %s read|lds|ldsmap|mfma\n", argv[0]);
   return 2;
 }

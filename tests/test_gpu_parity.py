@@ -467,6 +467,25 @@ def test_chunk_recompute_shape(torch_cuda, psplit):
         compare(db.out_numpy(), want, w.dtype, what=f"chunks split {psplit} rows {rows}")
 
 
+@pytest.mark.parametrize("nseq", [37, 300])
+@pytest.mark.parametrize("psplit", [0, 128])
+def test_many_multi_token_sequences(torch_cuda, nseq, psplit):
+    """Many short multi-token sequences (more than the planner's 256
+    threads), many with equal context lengths, whole and with split
+    contexts, on both tile sizes, against the oracle."""
+    from paged_kv_cache_block_amd import binding
+    rng = np.random.default_rng(nseq)
+    seqs = [(int(rng.choice([0, 9, 130, 131])), int(rng.integers(2, 6)), 1) for _ in range(nseq)]
+    w = build_batch(f"{nseq} multi-token f16", "f16", 8, 2, 64, 16, 10 * nseq + 8, seqs, 5)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    for rows in (128, 256):
+        say("multi-token sequences", nseq, "prefill split", psplit, "rows", rows)
+        db = run_gpu(w, binding.options(0, psplit, prefill_tile_rows=rows))
+        compare(db.out_numpy(), want, w.dtype, what=f"{nseq} seqs split {psplit} rows {rows}")
+
+
 def test_edge_cases(torch_cuda):
     """Sequences with no new tokens, one-token contexts, prefills without
     history, sub-requests sharing one block-table row, and a ragged tail."""
