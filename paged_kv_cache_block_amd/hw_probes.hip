@@ -12,6 +12,10 @@
 //   paged_kv_cache_block_amd/hw_probes mfma   32x32x16 bf16 MFMA rate, and how
 //                                             vector work overlaps it within one
 //                                             wave and across two waves of a SIMD
+//   paged_kv_cache_block_amd/hw_probes attnloop  an attention-shaped loop: per 32-key
+//                                             half, 8 dependent MFMAs from LDS
+//                                             operands, a softmax, 8 more MFMAs,
+//                                             with parts switched off
 //
 // Every kernel writes one output element per thread into a buffer sized for
 // its grid and reads only inside its own input buffer.
@@ -24,6 +28,7 @@
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define CK(x)                                                                         \
@@ -232,6 +237,98 @@ __global__ __launch_bounds__(512) void mfma_and_valu_waves(float* out, int it_mf
   out[blockIdx.x * 512 + threadIdx.x] = s;
 }
 
+// ---- attnloop --------------------------------------------------------------
+// 8 waves (two per SIMD), each repeating per 32-key half: 16 operand reads of
+// 1 KB from LDS, S = 8 dependent 32x32x16 MFMAs, a softmax over S (max,
+// exp2, bf16 packing, row sum) and 8 PV MFMAs into 4 accumulators: the
+// multi-token kernel's operand bytes and MFMAs per half.  MODE bit 0: a
+// barrier every 4 halves; bit 1: waves 4-7 start 8 MFMAs late; bit 2: no
+// softmax (S packed as is); bit 3: no MFMAs (vector work only).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <int MODE>
+__global__ __launch_bounds__(512) void attn_loop(float* out, int iters) {
+  constexpr bool BAR = MODE & 1, OFF = MODE & 2, NOSM = MODE & 4, NOM = MODE & 8;
+  __shared__ __attribute__((aligned(16))) u32x4 ops[2][16][64];   // two stages of 16 operands
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 2 * 16 * 64; i += 512) {
+    const uint32_t x = i * 2654435761u;
+    (&ops[0][0][0])[i] = u32x4{x, x * 3u, x * 5u, x * 7u} & 0x3c003c00u;   // small bf16 values
+  }
+  __syncthreads();
+  u32x4 q[8];
+  for (int k = 0; k < 8; ++k) q[k] = u32x4{lane * 3u + k, lane * 5u, lane * 7u, lane * 11u} & 0x3c003c00u;
+  f32x16 o[4] = {};
+  f32x16 dummy = {};
+  float m = 0.f, l = 0.f;
+  if (OFF && wv >= 4) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dummy = mfma(q[k], q[7 - k], dummy);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int it = 0; it < iters; ++it) {
+    const int st = it & 1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      u32x4 kop[8], vop[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        kop[k] = ops[st][(k + u) & 15][lane];
+        vop[k] = ops[st][(8 + k + u) & 15][lane ^ 32];
+      }
+      f32x16 s = {};
+      if (!NOM) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s = mfma(kop[k], q[k], s);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = __builtin_bit_cast(float, kop[e & 7][e >> 3]) * 1e-3f;
+      }
+      u32x4 pb[2];
+      if (!NOSM) {
+        float mx = s[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mu = fmaxf(m, mx);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], 0.0883f, -mu));
+        float rs = 0.f;
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pb[v2][w] = pack_bf16(s[8 * v2 + 2 * w], s[8 * v2 + 2 * w + 1]);
+            rs += s[8 * v2 + 2 * w] + s[8 * v2 + 2 * w + 1];
+          }
+        l += rs;
+        m = mu;
+      } else {
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pb[v2][w] = __builtin_bit_cast(uint32_t, s[8 * v2 + 2 * w]) & 0x3c003c00u;
+      }
+      if (!NOM) {
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[t] = mfma(vop[4 * v2 + t], pb[v2], o[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t][0] += __builtin_bit_cast(float, pb[t & 1][t]);
+      }
+    }
+    if (BAR) __syncthreads();
+  }
+  float r = m + l;
+  for (int t = 0; t < 4; ++t)
+    for (int e = 0; e < 16; ++e) r += o[t][e] + dummy[e];
+  out[blockIdx.x * 512 + threadIdx.x] = r;
+}
+
 struct Timer {
   hipEvent_t e0, e1;
   Timer() {
@@ -343,6 +440,29 @@ int probe_ldsmap(int cus) {
   return 0;
 }
 
+int probe_attnloop(int cus) {
+  float* out;
+  CK(hipMalloc(&out, sizeof(float) * 512 * (size_t)cus));
+  Timer t;
+  const int iters = 2000;
+  auto run = [&](const char* name, void (*k)(float*, int)) {
+    const float ms = t.best([&] { hipLaunchKernelGGL(k, dim3(cus), dim3(512), 0, 0, out, iters); });
+    const double slots = 2.0 * iters * 4 * 16;   // MFMA slots per SIMD: 2 waves x halves x 16
+    const double cyc = ms * 1e-3 * kNominalHz;
+    printf("attnloop %-40s %.3f ms, %.1f nominal cycles per MFMA slot, %.2f of the 32-cycle MFMA rate\n", name, ms,
+           cyc / slots, slots * 32 / cyc);
+  };
+  run("MFMAs + softmax", attn_loop<0>);
+  run("MFMAs + softmax, barrier per 4 halves", attn_loop<1>);
+  run("MFMAs + softmax, barrier, offset waves", attn_loop<3>);
+  run("MFMAs + softmax, offset waves", attn_loop<2>);
+  run("MFMAs only (operands from LDS)", attn_loop<4>);
+  run("MFMAs only, barrier", attn_loop<5>);
+  run("softmax only (operands from LDS)", attn_loop<8>);
+  CK(hipFree(out));
+  return 0;
+}
+
 int probe_mfma(int cus) {
   float* out;
   CK(hipMalloc(&out, sizeof(float) * 512 * (size_t)cus));
@@ -383,6 +503,7 @@ int main(int argc, char** argv) {
   if (!strcmp(mode, "lds")) return probe_lds(prop.multiProcessorCount);
   if (!strcmp(mode, "mfma")) return probe_mfma(prop.multiProcessorCount);
   if (!strcmp(mode, "ldsmap")) return probe_ldsmap(prop.multiProcessorCount);
-  fprintf(stderr, "usage: %s read|lds|ldsmap|mfma\n", argv[0]);
+  if (!strcmp(mode, "attnloop")) return probe_attnloop(prop.multiProcessorCount);
+  fprintf(stderr, "usage: %s read|lds|ldsmap|mfma|attnloop\n", argv[0]);
   return 2;
 }
