@@ -7,7 +7,8 @@ raises ``ImportError`` when it has not been built.  Build with
 ``python -m paged_kv_cache_block_amd.build``.
 """
 
-_API = ("pa_write_kv", "pa_copy_blocks", "pa_attention", "pa_attention_workspace_size",
+_API = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks",
+        "pa_attention", "pa_write_kv_attention", "pa_attention_workspace_size",
         "cache_desc", "options", "version", "PagedAttnError", "LIB_PATH")
 
 
