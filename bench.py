@@ -210,12 +210,13 @@ def chunk_cost(args) -> int:
                 nb = batch * ((L + bs - 1) // bs) + 8
                 w = build_batch(f"chunk {chunk} after {ctx}", "bf16", hq, hkv, d, bs, nb,
                                 [(ctx, chunk, 1)] * batch, 4242 + ctx)
-                psplit = 0
+                psplit, flags = 0, binding.PA_FLAG_KV_UNSHARED | binding.PA_FLAG_NO_PREFILL_SPLIT
                 if split_mode == "split":
                     items = batch * hkv           # one 256-row tile per chunk and KV head
                     want = max(1, -(-256 // items))
                     psplit = max(128, -(-L // want))
-                opt = binding.options(0, psplit, binding.PA_FLAG_KV_UNSHARED, prefill_tile_rows=256)
+                    flags = binding.PA_FLAG_KV_UNSHARED
+                opt = binding.options(0, psplit, flags, prefill_tile_rows=256)
                 db = DeviceBatch(w, opt=opt)
                 db.write_history()
                 db.write_new()
@@ -522,7 +523,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
     ap.add_argument("--prefill-split", type=int, default=0,
-                    help="keys per split of a multi-token context (0 = no split)")
+                    help="keys per split of a multi-token context (0 = auto, -1 = none)")
     ap.add_argument("--separate-write", action="store_true",
                     help="time pa_write_kv then pa_attention instead of pa_write_kv_attention")
     ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 128, 256],
@@ -571,6 +572,9 @@ def main(argv=None) -> int:
     print(f"[bench] built {w.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     unshared = blocks_unshared(w)
     flags = binding.PA_FLAG_KV_UNSHARED if unshared else 0
+    if args.prefill_split < 0:
+        flags |= binding.PA_FLAG_NO_PREFILL_SPLIT
+        args.prefill_split = 0
     db = DeviceBatch(w, opt=binding.options(args.split, args.prefill_split, flags, prefill_tile_rows=args.tile_rows))
     db.write_history()
     torch.cuda.synchronize()
@@ -652,7 +656,8 @@ def main(argv=None) -> int:
                 "algorithmic_flops": model["tile_flops"], "avg_ms": round(dom_ms, 5)}
     from paged_kv_cache_block_amd.profiling import traffic_record_for
     rec = (traffic_record_for(roof["kernel"], args.config)
-           if args.split == 0 and args.tile_rows == 0 and args.prefill_split == 0 else None)
+           if args.split == 0 and args.tile_rows == 0 and args.prefill_split == 0
+           and not flags & binding.PA_FLAG_NO_PREFILL_SPLIT else None)
     if rec is not None:
         roof["traffic"] = rec["fetch_bytes"] + rec["write_bytes"]
         roof["traffic_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "

@@ -86,10 +86,13 @@ typedef struct {
    * state that a combine kernel merges. */
   int32_t decode_split_tokens;
   /* Keys per split of a multi-token request's context, rounded up to a
-   * multiple of 128; 0 = no split.  Each (tile of rows, split) is a separate
+   * multiple of 128; 0 = auto.  Each (tile of rows, split) is a separate
    * work item; a new token whose causal range spans several splits gets one
    * partial softmax state per split, merged by the combine kernel (more
-   * parallelism for few, long requests).  The workspace size depends on it. */
+   * parallelism for few, long requests).  Auto splits only when some work
+   * item is longer than half a workgroup's share of the batch's multi-token
+   * work, into splits of at least 1024 keys; PA_FLAG_NO_PREFILL_SPLIT turns
+   * it off.  The workspace size depends on it. */
   int32_t prefill_split_tokens;
   /* Bit 0 (PA_FLAG_VECTOR_ALU): route every row through the vector-ALU row
    * kernel (the MFMA kernels are skipped).
@@ -98,6 +101,8 @@ typedef struct {
    * sub-requests over one table row).  Decode then streams K/V with
    * non-temporal loads, which is faster when nothing is re-read and slower
    * when blocks are shared; results are identical either way.
+   * Bit 2 (PA_FLAG_NO_PREFILL_SPLIT): with prefill_split_tokens = 0, never
+   * split multi-token contexts.
    * Other bits must be 0. */
   int32_t flags;
   /* Profiling hook: when timed_kernel is one of PA_TIME_* and that kernel is
@@ -113,7 +118,7 @@ typedef struct {
 } pa_options;
 
 enum { PA_TIME_NONE = 0, PA_TIME_TILE = 1, PA_TIME_ROWS = 2, PA_TIME_COMBINE = 3 };
-enum { PA_FLAG_VECTOR_ALU = 1, PA_FLAG_KV_UNSHARED = 2 };
+enum { PA_FLAG_VECTOR_ALU = 1, PA_FLAG_KV_UNSHARED = 2, PA_FLAG_NO_PREFILL_SPLIT = 4 };
 
 /*
  * pa_write_kv -- slot-mapping scatter of new K/V into the pools.

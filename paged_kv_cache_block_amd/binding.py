@@ -38,7 +38,7 @@ class PaOptions(ctypes.Structure):
 
 
 PA_TIME_NONE, PA_TIME_TILE, PA_TIME_ROWS, PA_TIME_COMBINE = 0, 1, 2, 3
-PA_FLAG_VECTOR_ALU, PA_FLAG_KV_UNSHARED = 1, 2
+PA_FLAG_VECTOR_ALU, PA_FLAG_KV_UNSHARED, PA_FLAG_NO_PREFILL_SPLIT = 1, 2, 4
 
 
 class PagedAttnError(RuntimeError):

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -77,11 +78,58 @@ int choose_split(const pa_options* opt, int64_t total_keys, int num_kv_heads, in
   return (int)std::min<int64_t>(kMaxAutoSplit, std::max<int64_t>(kMinAutoSplit, want));
 }
 
-// Keys per split of a multi-token sequence: the option rounded up to a whole
-// number of 128-key MFMA tiles; 0 = no split.
+// Keys per split of a multi-token sequence given by the option, rounded up to
+// a whole number of 128-key MFMA tiles; 0 = none given.
 int prefill_split(const pa_options* opt) {
   if (!opt || opt->prefill_split_tokens <= 0) return 0;
   return (opt->prefill_split_tokens + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum * kPrefillSplitQuantum;
+}
+
+// Automatic multi-token key split: with W keys of tile work over P resident
+// workgroups, splits of about W / (2P) keys (never fewer than
+// kMinAutoPrefillSplit, rounded to the quantum), used only when some tile
+// item is longer than that.  Shorter splits cost more in partial states and
+// their combine than they gain in balance.
+constexpr int kMinAutoPrefillSplit = 1024;
+
+bool auto_prefill_split(const pa_options* opt) {
+  return prefill_split(opt) == 0 && !(opt && (opt->flags & PA_FLAG_NO_PREFILL_SPLIT));
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Automatic key split of a batch's multi-token work (see kMinAutoPrefillSplit):
+// 0 when every tile item already fits in half a workgroup's share.
+int choose_prefill_split(const int32_t* lens, const int32_t* qsl, int num_seqs, int group,
+                         int tile_rows, int num_kv_heads) {
+  int64_t work = 0;
+  int longest = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = qsl[s + 1] - qsl[s];
+    const SeqWork w = seq_work(n, 0, group, tile_rows);
+    for (int t = 0; t < w.tiles; ++t) {
+      const int k = tile_key_end(n, lens[s], group, tile_rows, t);
+      work += k;
+      longest = std::max(longest, k);
+    }
+  }
+  if (work == 0) return 0;
+  const int64_t slots = (int64_t)cu_count() * (tile_rows == kTileRowsWide ? 1 : 2);
+  int64_t want = std::max<int64_t>(work * num_kv_heads / (2 * slots), kMinAutoPrefillSplit);
+  want = (want + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum * kPrefillSplitQuantum;
+  return longest > want ? (int)want : 0;
 }
 
 bool vector_all(const PoolArgs& p, const pa_options* opt) {
@@ -109,7 +157,8 @@ WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q
   w.cap_combs = row_rows;
   w.cap_partials = w.cap_rows;
   w.cap_tiles = va ? 0 : ((int64_t)total_q * group + kTileRows - 1) / kTileRows + num_seqs;
-  const int ps = prefill_split(opt);
+  // The automatic split is never shorter than kMinAutoPrefillSplit keys.
+  const int ps = auto_prefill_split(opt) ? kMinAutoPrefillSplit : prefill_split(opt);
   if (!va && ps > 0) {
     // Every tile has at most key_splits(max_len) splits; every new token at
     // most that many partial slots and one combine item.
@@ -393,7 +442,7 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not supported", group);
   if (num_seqs < 0 || total_q < 0) return fail(PA_ERR_INVALID_ARG, "negative num_seqs or total_q");
-  if (opt && (opt->flags & ~(PA_FLAG_VECTOR_ALU | PA_FLAG_KV_UNSHARED)))
+  if (opt && (opt->flags & ~(PA_FLAG_VECTOR_ALU | PA_FLAG_KV_UNSHARED | PA_FLAG_NO_PREFILL_SPLIT)))
     return fail(PA_ERR_INVALID_ARG, "unknown option flags");
   if (opt && (opt->decode_split_tokens < 0 || opt->prefill_split_tokens < 0))
     return fail(PA_ERR_INVALID_ARG, "negative split length");
@@ -481,7 +530,11 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
                        kTileRowsWide).tiles;
     if (wide * p.num_kv_heads >= kWideTileMinGroups) tile_rows = kTileRowsWide;
   }
-  const int psplit = va ? 0 : prefill_split(opt);
+  const int psplit = va ? 0
+                     : auto_prefill_split(opt)
+                         ? choose_prefill_split(context_lens_host, query_start_loc_host, num_seqs,
+                                                group, tile_rows, p.num_kv_heads)
+                         : prefill_split(opt);
   int64_t n_rows = 0, n_tiles = 0, n_combs = 0, n_partials = 0;
   for (int s = 0; s < num_seqs; ++s) {
     const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];

@@ -50,6 +50,13 @@ def test_workspace_size_is_host_only(binding):
     # so does splitting multi-token contexts
     psplit = binding.pa_attention_workspace_size(d, 40, 64, 64, 2048, binding.options(0, 512))
     assert psplit > n
+    # the default (automatic) multi-token split is never shorter than 1024
+    # keys, so its bound covers an explicit 1024-key split; without splits
+    # less room is needed
+    p1024 = binding.pa_attention_workspace_size(d, 40, 64, 64, 2048, binding.options(0, 1024))
+    nosplit = binding.pa_attention_workspace_size(
+        d, 40, 64, 64, 2048, binding.options(0, 0, binding.PA_FLAG_NO_PREFILL_SPLIT))
+    assert n >= p1024 > nosplit
     assert binding.pa_attention_workspace_size(d, 41, 64, 64, 2048) == 0   # 41 % 40 != 0
 
 
@@ -93,7 +100,7 @@ def test_attention_argument_errors(binding, case, expect):
     elif case == "workspace":
         ws = 10
     elif case == "flags":
-        opt = b.options(0, 0, 4)
+        opt = b.options(0, 0, 8)
     elif case == "neg_split":
         opt = b.options(0, -128)
     elif case == "block128_vector":   # fp32 rows take the vector-ALU kernel: no 128-token blocks

@@ -238,7 +238,7 @@ def test_write_kv_runs_and_gaps(torch_cuda, dtype, bs):
 
 
 @pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream", "tile128", "tile256",
-                                  "psplit128", "psplit128w"])
+                                  "psplit128", "psplit128w", "nopsplit"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_attention_small(torch_cuda, cfg, mode):
     from paged_kv_cache_block_amd import binding
@@ -248,7 +248,8 @@ def test_attention_small(torch_cuda, cfg, mode):
            "tile128": binding.options(prefill_tile_rows=128),
            "tile256": binding.options(prefill_tile_rows=256),
            "psplit128": binding.options(prefill_split_tokens=128),
-           "psplit128w": binding.options(prefill_split_tokens=128, prefill_tile_rows=256)}[mode]
+           "psplit128w": binding.options(prefill_split_tokens=128, prefill_tile_rows=256),
+           "nopsplit": binding.options(0, 0, binding.PA_FLAG_NO_PREFILL_SPLIT)}[mode]
     w = small_workload(cfg)
     say("attention", w.name, mode)
     db = run_gpu(w, opt)
@@ -451,10 +452,11 @@ def test_prefill_split_lengths_agree(torch_cuda, cfg):
                         what=f"{w.name} prefill split {psplit} rows {rows} decode split {dsplit}")
 
 
-@pytest.mark.parametrize("psplit", [0, 128, 1024])
+@pytest.mark.parametrize("psplit", [-1, 0, 128, 1024])
 def test_chunk_recompute_shape(torch_cuda, psplit):
     """32-token chunks after 0..3000 cached tokens (the chunk recomputation
-    the cost profile measures), whole and with split contexts."""
+    the cost profile measures), whole (-1), with the automatic split (0) and
+    with given split lengths."""
     from paged_kv_cache_block_amd import binding
     seqs = [(0, 32, 1), (31, 32, 1), (700, 32, 2), (3000, 32, 1)]
     w = build_batch("32-token chunks bf16", "bf16", 64, 8, 128, 32, 256, seqs, 77)
@@ -463,7 +465,9 @@ def test_chunk_recompute_shape(torch_cuda, psplit):
                             w.num_kv_heads, w.dtype, w.scale)
     for rows in (128, 256):
         say("chunk shape split", psplit, "rows", rows)
-        db = run_gpu(w, binding.options(0, psplit, prefill_tile_rows=rows))
+        opt = (binding.options(0, 0, binding.PA_FLAG_NO_PREFILL_SPLIT, prefill_tile_rows=rows)
+               if psplit < 0 else binding.options(0, psplit, prefill_tile_rows=rows))
+        db = run_gpu(w, opt)
         compare(db.out_numpy(), want, w.dtype, what=f"chunks split {psplit} rows {rows}")
 
 
