@@ -203,7 +203,7 @@ def chunk_cost(args) -> int:
     reps = max(args.steps, 5)
     rows = []
     for batch, ctxs in ((1, contexts), (16, contexts[:6])):
-        for split_mode in ("none", "split"):
+        for split_mode in ("none", "auto", "split"):
             times = []
             for ctx in ctxs:
                 L = ctx + chunk
@@ -211,6 +211,8 @@ def chunk_cost(args) -> int:
                 w = build_batch(f"chunk {chunk} after {ctx}", "bf16", hq, hkv, d, bs, nb,
                                 [(ctx, chunk, 1)] * batch, 4242 + ctx)
                 psplit, flags = 0, binding.PA_FLAG_KV_UNSHARED | binding.PA_FLAG_NO_PREFILL_SPLIT
+                if split_mode == "auto":      # the library's own choice
+                    flags = binding.PA_FLAG_KV_UNSHARED
                 if split_mode == "split":
                     items = batch * hkv           # one 256-row tile per chunk and KV head
                     want = max(1, -(-256 // items))
@@ -233,6 +235,7 @@ def chunk_cost(args) -> int:
                 flops = 4 * d * hq * batch * (chunk * ctx + chunk * (chunk + 1) // 2)
                 times.append(us)
                 line = {"chunk_cost": {"chunk": chunk, "context": ctx, "batch": batch,
+                                       "split_mode": split_mode,
                                        "prefill_split": psplit, "us": round(us, 2),
                                        "us_per_chunk": round(us / batch, 2),
                                        "tflops": round(flops / us / 1e6, 1)}}

@@ -89,10 +89,12 @@ typedef struct {
    * multiple of 128; 0 = auto.  Each (tile of rows, split) is a separate
    * work item; a new token whose causal range spans several splits gets one
    * partial softmax state per split, merged by the combine kernel (more
-   * parallelism for few, long requests).  Auto splits only when some work
-   * item is longer than half a workgroup's share of the batch's multi-token
-   * work, into splits of at least 1024 keys; PA_FLAG_NO_PREFILL_SPLIT turns
-   * it off.  The workspace size depends on it. */
+   * parallelism for few, long requests).  Auto cuts the longest work item
+   * into equal splits of about half a workgroup's share of the batch's
+   * multi-token work (at least 1024 keys, or 256 when the unsplit items fill
+   * under a quarter of the GPU's workgroup slots), and only when that makes
+   * two splits or more; PA_FLAG_NO_PREFILL_SPLIT turns it off.  The
+   * workspace size depends on it. */
   int32_t prefill_split_tokens;
   /* Bit 0 (PA_FLAG_VECTOR_ALU): route every row through the vector-ALU row
    * kernel (the MFMA kernels are skipped).

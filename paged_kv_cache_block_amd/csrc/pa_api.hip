@@ -86,11 +86,17 @@ int prefill_split(const pa_options* opt) {
 }
 
 // Automatic multi-token key split: with W keys of tile work over P resident
-// workgroups, splits of about W / (2P) keys (never fewer than
-// kMinAutoPrefillSplit, rounded to the quantum), used only when some tile
-// item is longer than that.  Shorter splits cost more in partial states and
-// their combine than they gain in balance.
+// workgroups, a target of w = max(W / (2P), floor) keys per split.  The
+// longest item is cut into floor(longest / w) equal splits (rounded up to the
+// quantum), and nothing is split when that is fewer than two: a split that
+// only trims an item costs its partial states and their combine without
+// shortening the launch.  Nor is an item cut into more pieces than make the
+// batch's items fill the workgroup slots once (two pieces are always
+// allowed).  The floor is kMinAutoPrefillSplit, or kMinAutoPrefillSplitSparse
+// when the unsplit items fill less than a quarter of the slots (then
+// parallelism outweighs the partial states).
 constexpr int kMinAutoPrefillSplit = 1024;
+constexpr int kMinAutoPrefillSplitSparse = 256;
 
 bool auto_prefill_split(const pa_options* opt) {
   return prefill_split(opt) == 0 && !(opt && (opt->flags & PA_FLAG_NO_PREFILL_SPLIT));
@@ -111,14 +117,15 @@ int cu_count() {
 }
 
 // Automatic key split of a batch's multi-token work (see kMinAutoPrefillSplit):
-// 0 when every tile item already fits in half a workgroup's share.
+// 0 when the longest item is shorter than two target splits.
 int choose_prefill_split(const int32_t* lens, const int32_t* qsl, int num_seqs, int group,
                          int tile_rows, int num_kv_heads) {
-  int64_t work = 0;
+  int64_t work = 0, items = 0;
   int longest = 0;
   for (int s = 0; s < num_seqs; ++s) {
     const int n = qsl[s + 1] - qsl[s];
     const SeqWork w = seq_work(n, 0, group, tile_rows);
+    items += w.tiles;
     for (int t = 0; t < w.tiles; ++t) {
       const int k = tile_key_end(n, lens[s], group, tile_rows, t);
       work += k;
@@ -127,9 +134,17 @@ int choose_prefill_split(const int32_t* lens, const int32_t* qsl, int num_seqs, 
   }
   if (work == 0) return 0;
   const int64_t slots = (int64_t)cu_count() * (tile_rows == kTileRowsWide ? 1 : 2);
-  int64_t want = std::max<int64_t>(work * num_kv_heads / (2 * slots), kMinAutoPrefillSplit);
-  want = (want + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum * kPrefillSplitQuantum;
-  return longest > want ? (int)want : 0;
+  const bool sparse = items * num_kv_heads * 4 < slots;
+  const int64_t want = std::max<int64_t>(work * num_kv_heads / (2 * slots),
+                                         sparse ? kMinAutoPrefillSplitSparse : kMinAutoPrefillSplit);
+  // Split up to filling the slots once, not beyond (more items than slots
+  // add a round and more partial states to combine), but at least in two
+  // where the longest item is that much longer than the target.
+  const int64_t pieces =
+      std::min<int64_t>(longest / want, std::max<int64_t>(2, slots / (items * num_kv_heads)));
+  if (pieces < 2) return 0;
+  const int64_t split = (longest + pieces - 1) / pieces;
+  return (int)((split + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum * kPrefillSplitQuantum);
 }
 
 bool vector_all(const PoolArgs& p, const pa_options* opt) {
@@ -157,7 +172,8 @@ WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q
   w.cap_combs = row_rows;
   w.cap_partials = w.cap_rows;
   w.cap_tiles = va ? 0 : ((int64_t)total_q * group + kTileRows - 1) / kTileRows + num_seqs;
-  // The automatic split is never shorter than kMinAutoPrefillSplit keys.
+  // Room for automatic splits of kMinAutoPrefillSplit keys; shorter ones are
+  // lengthened at call time until they fit.
   const int ps = auto_prefill_split(opt) ? kMinAutoPrefillSplit : prefill_split(opt);
   if (!va && ps > 0) {
     // Every tile has at most key_splits(max_len) splits; every new token at
@@ -530,32 +546,45 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
                        kTileRowsWide).tiles;
     if (wide * p.num_kv_heads >= kWideTileMinGroups) tile_rows = kTileRowsWide;
   }
-  const int psplit = va ? 0
-                     : auto_prefill_split(opt)
-                         ? choose_prefill_split(context_lens_host, query_start_loc_host, num_seqs,
-                                                group, tile_rows, p.num_kv_heads)
-                         : prefill_split(opt);
+  int psplit = va ? 0
+               : auto_prefill_split(opt)
+                   ? choose_prefill_split(context_lens_host, query_start_loc_host, num_seqs,
+                                          group, tile_rows, p.num_kv_heads)
+                   : prefill_split(opt);
   int64_t n_rows = 0, n_tiles = 0, n_combs = 0, n_partials = 0;
-  for (int s = 0; s < num_seqs; ++s) {
-    const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
-    const int L = context_lens_host[s];
-    const SeqWork w = seq_work(n, va ? 1 : 0, group, tile_rows);
-    for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
-      const int ns = row_splits(L - n + i + 1, split);
-      n_rows += ns;
-      if (ns > 1) {
-        n_combs += 1;
-        n_partials += ns;
+  auto count = [&]() {
+    n_rows = n_tiles = n_combs = n_partials = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
+      const int L = context_lens_host[s];
+      const SeqWork w = seq_work(n, va ? 1 : 0, group, tile_rows);
+      for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
+        const int ns = row_splits(L - n + i + 1, split);
+        n_rows += ns;
+        if (ns > 1) {
+          n_combs += 1;
+          n_partials += ns;
+        }
       }
+      const TileWork tw = tile_work(n, L, group, tile_rows, w.tiles, psplit);
+      n_tiles += tw.items;
+      n_combs += tw.combs;
+      n_partials += tw.slots;
     }
-    const TileWork tw = tile_work(n, L, group, tile_rows, w.tiles, psplit);
-    n_tiles += tw.items;
-    n_combs += tw.combs;
-    n_partials += tw.slots;
+    return n_rows <= lay.cap_rows && n_tiles <= lay.cap_tiles && n_combs <= lay.cap_combs &&
+           n_partials <= lay.cap_partials;
+  };
+  bool fits = count();
+  // The workspace bound assumes automatic splits of at least
+  // kMinAutoPrefillSplit keys; a shorter (sparse-grid) split that does not
+  // fit is lengthened until it does.
+  while (!fits && psplit > 0 && auto_prefill_split(opt)) {
+    const int longer = (psplit + psplit / 4 + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum *
+                       kPrefillSplitQuantum;
+    psplit = psplit >= max_len ? 0 : std::max(longer, psplit + kPrefillSplitQuantum);
+    fits = count();
   }
-  if (n_rows > lay.cap_rows || n_tiles > lay.cap_tiles || n_combs > lay.cap_combs ||
-      n_partials > lay.cap_partials)
-    return fail(PA_ERR_WORKSPACE, "plan exceeds workspace capacity");
+  if (!fits) return fail(PA_ERR_WORKSPACE, "plan exceeds workspace capacity");
   if (n_rows > 0x7fffffff || n_tiles > 0x7fffffff)
     return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
   const bool rows_on_mfma = !va && decode_mfma_supported(p, group);
