@@ -490,6 +490,61 @@ def test_many_multi_token_sequences(torch_cuda, nseq, psplit):
         compare(db.out_numpy(), want, w.dtype, what=f"{nseq} seqs split {psplit} rows {rows}")
 
 
+def _random_batch_spec(seed):
+    """A seeded random batch: dtype, head dim, block size, GQA group, and a
+    mix of decode rows, prompts, prompts after history (some on two block
+    runs) and sequences without new tokens, with one option set."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = str(rng.choice(["f16", "bf16", "f32"]))
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([4, 8, 16, 32, 64] + ([128] if dtype != "f32" else [])))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    seqs = []
+    for _ in range(int(rng.integers(1, 10))):
+        kind = rng.choice(["decode", "prefill", "mixed", "empty"], p=[0.4, 0.2, 0.3, 0.1])
+        if kind == "decode":
+            h, n = int(rng.integers(0, 700)), 1
+        elif kind == "prefill":
+            h, n = 0, int(rng.integers(2, 81))
+        elif kind == "mixed":
+            h, n = int(rng.integers(1, 500)), int(rng.integers(2, 49))
+        else:
+            h, n = int(rng.integers(1, 300)), 0
+        seqs.append((h, n, 2 if h >= 2 * bs and rng.random() < 0.3 else 1))
+    mode = str(rng.choice(["default", "split64", "psplit128", "nopsplit", "tile128", "tile256",
+                           "rows", "stream"]))
+    if bs == 128 and mode == "rows":     # 128-token blocks have no vector-ALU path
+        mode = "default"
+    nblocks = 2 * sum(-(-(h + n) // bs) for h, n, _ in seqs) + 64
+    return dtype, d, bs, hkv, g, seqs, mode, nblocks
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_batches(torch_cuda, seed):
+    """Seeded random batches over the supported shapes and options, against
+    the oracle."""
+    from paged_kv_cache_block_amd import binding
+    dtype, d, bs, hkv, g, seqs, mode, nblocks = _random_batch_spec(seed)
+    opt = {"default": None, "split64": binding.options(64),
+           "psplit128": binding.options(prefill_split_tokens=128),
+           "nopsplit": binding.options(0, 0, binding.PA_FLAG_NO_PREFILL_SPLIT),
+           "tile128": binding.options(prefill_tile_rows=128),
+           "tile256": binding.options(prefill_tile_rows=256),
+           "rows": binding.options(0, 0, binding.PA_FLAG_VECTOR_ALU),
+           "stream": binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED)}[mode]
+    w = build_batch(f"random {seed}", dtype, hkv * g, hkv, d, bs, nblocks, seqs, seed)
+    say("random", seed, dtype, "D", d, "bs", bs, "H", hkv * g, "/", hkv, "seqs", seqs, mode)
+    db = run_gpu(w, opt)
+    if int(w.query_start_loc[-1]) == 0:   # no new tokens anywhere: nothing to attend
+        assert db.out_numpy().size == 0
+        return
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    compare(db.out_numpy(), want, w.dtype, what=f"random {seed} [{mode}]")
+
+
 def test_edge_cases(torch_cuda):
     """Sequences with no new tokens, one-token contexts, prefills without
     history, sub-requests sharing one block-table row, and a ragged tail."""
