@@ -80,14 +80,20 @@ __device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
 }
 
 // Key (within a 32-key half tile) held by accumulator element e of lane half hh.
-__device__ __forceinline__ int acc_key(int e, int hh) { return 16 * (e >> 3) + 8 * hh + (e & 7); }
+constexpr __host__ __device__ int acc_key(int e, int hh) { return 16 * (e >> 3) + 8 * hh + (e & 7); }
 
 // Key whose K row is loaded as row r of the S^T product.  Row r of a 32x32
 // accumulator lands in element 4*(r>>3) + (r&3) of lane half (r>>2)&1; this
 // map sends it to acc_key of that element.
-__device__ __forceinline__ int row_key(int r) {
+constexpr __host__ __device__ int row_key(int r) {
   return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
 }
+constexpr bool row_key_matches_acc_key() {
+  for (int r = 0; r < 32; ++r)
+    if (row_key(r) != acc_key(4 * (r >> 3) + (r & 3), (r >> 2) & 1)) return false;
+  return true;
+}
+static_assert(row_key_matches_acc_key(), "K row order must match the accumulator layout");
 
 // NW = waves per workgroup (4 or 8), 32 rows each: the K/V tile staged in
 // LDS serves 32 * NW rows, so larger workgroups issue fewer loads and LDS
