@@ -527,6 +527,8 @@ def main(argv=None) -> int:
     ap.add_argument("--split", type=int, default=0, help="decode split length (0 = auto)")
     ap.add_argument("--prefill-split", type=int, default=0,
                     help="keys per split of a multi-token context (0 = auto, -1 = none)")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="also time the dominant kernel with L2 and MALL flushed before each step")
     ap.add_argument("--separate-write", action="store_true",
                     help="time pa_write_kv then pa_attention instead of pa_write_kv_attention")
     ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 128, 256],
@@ -638,20 +640,22 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         per_kernel[name] = float(np.mean([a.elapsed_time(b) for a, b in evs2]))
 
-    # The dominant kernel once more with L2 and the MALL flushed before every
-    # step (a 512 MiB write between steps), as a cold-cache reference.  The
-    # timed steps above run back to back, as a serving loop does.
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=db.device)
-    evs3 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(K)]
-    opts3 = [binding.options(args.split, args.prefill_split, flags, dom_id, a, b, args.tile_rows)
-             for a, b in evs3]
-    for i in range(K):
-        scratch.fill_(i & 255)
-        run_step(opts3[i])
-    torch.cuda.synchronize()
-    dom_cold_ms = float(np.mean([a.elapsed_time(b) for a, b in evs3]))
-    del scratch
+    # --cold-cache: the dominant kernel once more with L2 and the MALL flushed
+    # before every step (a 512 MiB write between steps).  The timed steps
+    # above run back to back, as a serving loop does.
+    dom_cold_ms = None
+    if args.cold_cache:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=db.device)
+        evs3 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(K)]
+        opts3 = [binding.options(args.split, args.prefill_split, flags, dom_id, a, b, args.tile_rows)
+                 for a, b in evs3]
+        for i in range(K):
+            scratch.fill_(i & 255)
+            run_step(opts3[i])
+        torch.cuda.synchronize()
+        dom_cold_ms = float(np.mean([a.elapsed_time(b) for a, b in evs3]))
+        del scratch
 
     value = model["step_bytes"] / (ms_step * 1e-3) / 1e9
     rows_kernel = ("decode_mfma_kernel" if w.dtype != "f32" and w.block_size in (16, 32)
@@ -680,11 +684,12 @@ def main(argv=None) -> int:
         roof["traffic"] = rec["fetch_bytes"] + rec["write_bytes"]
         roof["traffic_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                 "scaled by pa_copy_blocks over a known byte count")
-    unit_work = model["rows_bytes"] if dominant == "rows" else model["tile_flops"]
-    roof["cold_cache"] = {
-        "avg_ms": round(dom_cold_ms, 5),
-        "achieved": round(unit_work / (dom_cold_ms * 1e-3) / (1e9 if dominant == "rows" else 1e12), 1),
-        "note": "the same kernel with a 512 MiB write before every step (L2 and MALL flushed)"}
+    if dom_cold_ms is not None:
+        unit_work = model["rows_bytes"] if dominant == "rows" else model["tile_flops"]
+        roof["cold_cache"] = {
+            "avg_ms": round(dom_cold_ms, 5),
+            "achieved": round(unit_work / (dom_cold_ms * 1e-3) / (1e9 if dominant == "rows" else 1e12), 1),
+            "note": "the same kernel with a 512 MiB write before every step (L2 and MALL flushed)"}
     extra = {}
     if "tile" in per_kernel:
         extra["multi_token_tflops"] = round(model["tile_flops"] / (per_kernel["tile"] * 1e-3) / 1e12, 1)

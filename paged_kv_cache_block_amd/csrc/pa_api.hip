@@ -11,7 +11,7 @@
 #include <string>
 #include <vector>
 
-#include "pa_internal.h"
+#include "pa_write.h"
 #include "pagedattn.h"
 
 using namespace pa;
@@ -247,6 +247,8 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
+  if (write_geom(num_tokens, p).chunks > 0x7fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "too many new tokens for one write (at most 2^31 - 1 16-byte chunks)");
   if (validate_mode()) {
     std::vector<int64_t> slots;
     if ((st = check_slots(slots, slot_mapping, num_tokens, p, stream)) != PA_OK) return st;
@@ -497,6 +499,8 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (fw && (!aligned16(fw->k_new) || !aligned16(fw->v_new)))
     return fail(PA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
+  if (fw && write_geom(total_q, p).chunks > 0x7fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "too many new tokens for one write (at most 2^31 - 1 16-byte chunks)");
 
   const WorkspaceLayout lay = make_layout(p, num_q_heads, num_seqs, total_q, max_len, opt);
   if (!workspace || workspace_bytes < lay.total)

@@ -135,7 +135,7 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, const int64_t* 
   const int eb = wg.eb, cpr = wg.cpr;
   const int64_t chunks = wg.chunks, blocks = wg.blocks, total_slots = wg.total_slots;
   if (chunks == 0) return hipSuccess;
-  if (2 * blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (chunks > 0x7fffffff) return hipErrorInvalidValue;   // 32-bit index arithmetic
   const dim3 grid((unsigned)(2 * blocks));
   if (eb == 4)
     hipLaunchKernelGGL(write_kv_kernel<4>, grid, dim3(256), 0, s, (const uint4*)k_new,

@@ -177,7 +177,7 @@ hipError_t launch_plan_write(const int32_t* context_lens, const int32_t* qsl, co
                              const void* v_new, const int64_t* slots, int num_tokens,
                              void* k_cache, void* v_cache, const PoolArgs& p, hipStream_t s) {
   const WriteGeom g = write_geom(num_tokens, p);
-  if (1 + 2 * g.blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (g.chunks > 0x7fffffff) return hipErrorInvalidValue;   // 32-bit index arithmetic
   const WriteArgs w{(const uint4*)k_new, (const uint4*)v_new, slots, (int64_t)num_tokens, g.chunks,
                     g.total_slots, (int)g.blocks, g.cpr, p.num_kv_heads, p.head_dim, p.block_size,
                     (uint8_t*)k_cache, v_cache};
