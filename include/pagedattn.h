@@ -137,7 +137,11 @@ enum { PA_FLAG_VECTOR_ALU = 1, PA_FLAG_KV_UNSHARED = 2, PA_FLAG_NO_PREFILL_SPLIT
  *                 skipped too (PA_VALIDATE=1 reports them as PA_ERR_BOUNDS).
  *  k_cache, v_cache  device pools (layout above), written in place.
  *  Precondition: slots within one call are distinct.  The copy is bit-exact.
- *  num_tokens == 0 is valid and enqueues nothing.
+ *  num_tokens == 0 is valid and enqueues nothing.  A call moves at most
+ *  2^31 - 1 16-byte chunks of K (num_tokens rounded up to 32, times
+ *  num_kv_heads times head_dim * elt / 16); beyond that it returns
+ *  PA_ERR_UNSUPPORTED (split the call).  pa_write_kv_attention has the same
+ *  limit for its total_q new tokens.
  */
 pa_status pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                       int32_t num_tokens, void* k_cache, void* v_cache,
