@@ -149,6 +149,11 @@ def test_write_and_copy_argument_errors(binding):
     assert b.LIB.pa_write_kv(None, None, None, 3, None, None, ctypes.byref(desc), None) == -1
     assert b.LIB.pa_write_kv(16, 16, 16, -1, 16, 16, ctypes.byref(desc), None) == -1
     assert b.LIB.pa_write_kv(8, 16, 16, 2, 16, 16, ctypes.byref(desc), None) == -1   # misaligned
+    # more than 2^31 - 1 16-byte chunks in one call: refused on the host
+    cpr = desc.head_dim * (4 if desc.dtype == 0 else 2) // 16
+    big = (1 << 31) // (desc.num_kv_heads * cpr) + 32
+    assert b.LIB.pa_write_kv(16, 16, 16, big, 16, 16, ctypes.byref(desc), None) == -2
+    assert b"too many new tokens" in b.LIB.pa_last_error()
     assert b.LIB.pa_copy_blocks(None, None, ctypes.byref(desc), None, 0, None) == 0
     assert b.LIB.pa_copy_blocks(None, None, ctypes.byref(desc), None, 2, None) == -1
     desc.block_size = 3
