@@ -329,6 +329,113 @@ __global__ __launch_bounds__(512) void attn_loop(float* out, int iters) {
   out[blockIdx.x * 512 + threadIdx.x] = r;
 }
 
+// The same loop with the multi-token kernel's other parts switched on: 64 KB
+// LDS stages (each half reads its own 16 operands), a barrier every 4 halves,
+// and MODE bit 0: the kernel's softmax (a row max raised only past 2^8
+// behind a wave-wide ballot and branch, cross-lane steps by permlane, row
+// sums by v_dot2 over the packed probabilities unless bit 3 asks for fp32
+// adds); bit 1: 8 16-byte global loads per thread per 4 halves from an
+// L2-resident 2 MB buffer; bit 2: their stores into the other LDS stage.
+template <int MODE>
+__global__ __launch_bounds__(512) void attn_stage(const u32x4* __restrict__ src, float* out, int iters) {
+  constexpr bool RS = MODE & 1, LD = MODE & 2, STO = MODE & 4, ADDS = MODE & 8;
+  extern __shared__ __attribute__((aligned(16))) u32x4 ops[];   // 2 stages x 64 operands x 64 lanes
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  for (int i = tid; i < 2 * 64 * 64; i += 512) {
+    const uint32_t x = i * 2654435761u;
+    ops[i] = u32x4{x, x * 3u, x * 5u, x * 7u} & 0x3c003c00u;
+  }
+  __syncthreads();
+  u32x4 q[8];
+  for (int k = 0; k < 8; ++k) q[k] = u32x4{lane * 3u + k, lane * 5u, lane * 7u, lane * 11u} & 0x3c003c00u;
+  f32x16 o[4] = {};
+  float m_run = -INFINITY, l_run = 0.f;
+  u32x4 buf[8];
+  for (int j = 0; j < 8; ++j) buf[j] = u32x4{0, 0, 0, 0};
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  for (int it = 0; it < iters; ++it) {
+    const int st = it & 1;
+    const u32x4* stg = ops + st * 64 * 64;
+    if (LD) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) buf[j] = src[((it & 31) * 8 + j) * 512 + tid] & 0x3c003c00u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      u32x4 kop[8], vop[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        kop[k] = stg[(16 * u + k) * 64 + lane];
+        vop[k] = stg[(16 * u + 8 + k) * 64 + lane];
+      }
+      f32x16 s = {};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s = mfma(kop[k], q[k], s);
+      u32x4 pb[2];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      float rs = 0.f;
+      if (RS) {
+        const uint32_t mu = __float_as_uint(mx);
+        const auto sw = __builtin_amdgcn_permlane32_swap(mu, mu, false, false);
+        const float m_cand = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * 0.0883f;
+        const bool raise = m_cand > m_run + 8.f;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float m_new = raise ? m_cand : m_run;
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[t] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], 0.0883f, -m_use));
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pb[v2][w] = pack_bf16(s[8 * v2 + 2 * w], s[8 * v2 + 2 * w + 1]);
+            if (ADDS) rs += s[8 * v2 + 2 * w] + s[8 * v2 + 2 * w + 1];
+            else rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[v2][w]), one, rs, false);
+          }
+        const uint32_t ru = __float_as_uint(rs);
+        const auto rw = __builtin_amdgcn_permlane32_swap(ru, ru, false, false);
+        l_run += __uint_as_float(rw[0]) + __uint_as_float(rw[1]);
+      } else {
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mu = fmaxf(m_run, mx);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], 0.0883f, -mu));
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            pb[v2][w] = pack_bf16(s[8 * v2 + 2 * w], s[8 * v2 + 2 * w + 1]);
+            rs += s[8 * v2 + 2 * w] + s[8 * v2 + 2 * w + 1];
+          }
+        l_run += rs;
+        m_run = mu;
+      }
+#pragma unroll
+      for (int v2 = 0; v2 < 2; ++v2)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = mfma(vop[4 * v2 + t], pb[v2], o[t]);
+    }
+    if (STO) {
+      u32x4* dst = ops + (st ^ 1) * 64 * 64;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j * 512 + tid] = buf[j];
+    }
+    __syncthreads();
+  }
+  float r = m_run + l_run;
+  for (int t = 0; t < 4; ++t)
+    for (int e = 0; e < 16; ++e) r += o[t][e];
+  out[blockIdx.x * 512 + threadIdx.x] = r;
+}
+
 struct Timer {
   hipEvent_t e0, e1;
   Timer() {
@@ -459,6 +566,29 @@ int probe_attnloop(int cus) {
   run("MFMAs only (operands from LDS)", attn_loop<4>);
   run("MFMAs only, barrier", attn_loop<5>);
   run("softmax only (operands from LDS)", attn_loop<8>);
+  // The kernel's parts, with 64 KB stages and a barrier every 4 halves.
+  u32x4* src;
+  const size_t src_bytes = (size_t)32 * 8 * 512 * 16;   // 2 MB, stays in L2
+  CK(hipMalloc(&src, src_bytes));
+  CK(hipMemset(src, 0, src_bytes));
+  const size_t lds = 2 * 64 * 64 * 16;
+  auto run2 = [&](const char* name, void (*k)(const u32x4*, float*, int)) -> int {
+    CK(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    const float ms = t.best([&] { hipLaunchKernelGGL(k, dim3(cus), dim3(512), lds, 0, src, out, iters); });
+    const double slots = 2.0 * iters * 4 * 16;
+    const double cyc = ms * 1e-3 * kNominalHz;
+    printf("attnloop %-40s %.3f ms, %.1f nominal cycles per MFMA slot, %.2f of the 32-cycle MFMA rate\n", name, ms,
+           cyc / slots, slots * 32 / cyc);
+    return 0;
+  };
+  if (run2("64 KB stages, simple softmax", attn_stage<0>)) return 1;
+  if (run2("+ kernel softmax (dot2 row sums)", attn_stage<1>)) return 1;
+  if (run2("+ kernel softmax (fp32 row sums)", attn_stage<1 | 8>)) return 1;
+  if (run2("+ tile loads", attn_stage<2>)) return 1;
+  if (run2("+ tile loads and LDS stores", attn_stage<2 | 4>)) return 1;
+  if (run2("+ LDS stores only", attn_stage<4>)) return 1;
+  if (run2("+ kernel softmax (fp32), loads, stores", attn_stage<1 | 2 | 4 | 8>)) return 1;
+  CK(hipFree(src));
   CK(hipFree(out));
   return 0;
 }
