@@ -90,24 +90,31 @@ def cpu_baseline(w, target_s: float):
     order = np.random.default_rng(0).permutation(w.num_seqs)
     kvb = w.kv_bytes_per_token()
     elt = ELT[w.dtype]
-    done, nbytes, nflops, t_used = [], 0, 0, 0.0
-    for s in order:
-        n = int(w.n_new[s])
-        if n == 0:
-            continue
-        t0 = time.perf_counter()
-        oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
-                         w.num_kv_heads, w.dtype, w.scale, seqs=[int(s)])
-        t_used += time.perf_counter() - t0
-        L = int(w.context_lens[s])
-        done.append(int(s))
-        nbytes += L * kvb + 2 * n * w.num_q_heads * w.head_dim * elt
-        nflops += 4 * w.head_dim * w.num_q_heads * (n * (L - n) + n * (n + 1) // 2)
-        if t_used >= target_s:
-            break
+    # Sequences in a seeded order, passing over the batch again while the
+    # time used is short of the target (a small batch is timed several times).
+    done, nbytes, nflops, t_used, passes = [], 0, 0, 0.0, 0
+    while t_used < target_s and passes < 50:
+        passes += 1
+        for s in order:
+            n = int(w.n_new[s])
+            if n == 0:
+                continue
+            t0 = time.perf_counter()
+            oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                             w.num_kv_heads, w.dtype, w.scale, seqs=[int(s)])
+            t_used += time.perf_counter() - t0
+            L = int(w.context_lens[s])
+            done.append(int(s))
+            nbytes += L * kvb + 2 * n * w.num_q_heads * w.head_dim * elt
+            nflops += 4 * w.head_dim * w.num_q_heads * (n * (L - n) + n * (n + 1) // 2)
+            if t_used >= target_s:
+                break
+    if not done:
+        return None
     return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle attention over {len(done)} of {w.num_seqs} sequences "
-                      f"({nbytes / 1e6:.1f} MB KV+q+out, {nflops / 1e9:.2f} GFLOP) in {t_used:.1f} s",
+            "sample": f"oracle attention, {len(done)} sequence evaluations over {len(set(done))} of "
+                      f"{w.num_seqs} sequences in {passes} pass(es) ({nbytes / 1e6:.1f} MB KV+q+out, "
+                      f"{nflops / 1e9:.2f} GFLOP) in {t_used:.2f} s",
             "gflops": nflops / t_used / 1e9}
 
 
@@ -701,7 +708,8 @@ def main(argv=None) -> int:
         t0 = time.time()
         cpu = cpu_baseline(w, args.cpu_seconds)
         print(f"[bench] cpu baseline in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
-        cpu = {k2: (round(v, 3) if isinstance(v, float) else v) for k2, v in cpu.items()}
+        if cpu is not None:
+            cpu = {k2: (round(v, 3) if isinstance(v, float) else v) for k2, v in cpu.items()}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
