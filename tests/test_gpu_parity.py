@@ -493,7 +493,8 @@ def test_many_multi_token_sequences(torch_cuda, nseq, psplit):
 def _random_batch_spec(seed):
     """A seeded random batch: dtype, head dim, block size, GQA group, and a
     mix of decode rows, prompts, prompts after history (some on two block
-    runs) and sequences without new tokens, with one option set."""
+    runs), sequences without new tokens and a few long histories, with one
+    option set."""
     rng = np.random.default_rng(1000 + seed)
     dtype = str(rng.choice(["f16", "bf16", "f32"]))
     d = int(rng.choice([64, 128]))
@@ -502,8 +503,10 @@ def _random_batch_spec(seed):
     g = int(rng.choice([1, 2, 4, 8, 16]))
     seqs = []
     for _ in range(int(rng.integers(1, 10))):
-        kind = rng.choice(["decode", "prefill", "mixed", "empty"], p=[0.4, 0.2, 0.3, 0.1])
-        if kind == "decode":
+        kind = rng.choice(["decode", "prefill", "mixed", "empty", "long"], p=[0.38, 0.2, 0.3, 0.07, 0.05])
+        if kind == "long":     # a long history: automatic key splits of decode rows and tiles
+            h, n = int(rng.integers(1000, 6000)), int(rng.choice([1, int(rng.integers(2, 33))]))
+        elif kind == "decode":
             h, n = int(rng.integers(0, 700)), 1
         elif kind == "prefill":
             h, n = 0, int(rng.integers(2, 81))
@@ -520,10 +523,10 @@ def _random_batch_spec(seed):
     return dtype, d, bs, hkv, g, seqs, mode, nblocks
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(int(os.environ.get("PA_RANDOM_SEEDS", "48"))))
 def test_random_batches(torch_cuda, seed):
     """Seeded random batches over the supported shapes and options, against
-    the oracle."""
+    the oracle (48 seeds; PA_RANDOM_SEEDS=N runs seeds 0..N-1)."""
     from paged_kv_cache_block_amd import binding
     dtype, d, bs, hkv, g, seqs, mode, nblocks = _random_batch_spec(seed)
     opt = {"default": None, "split64": binding.options(64),
