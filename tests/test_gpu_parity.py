@@ -237,6 +237,43 @@ def test_write_kv_runs_and_gaps(torch_cuda, dtype, bs):
     assert np.array_equal(bits(v0), bits(ve))
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_copy_and_write(torch_cuda, seed):
+    """Seeded random pools, copy-on-write pairs and slot mappings (distinct
+    slots in any order, some negative) over dtypes, head counts, head dims
+    and block sizes: copy then write, bit-exact against the oracle."""
+    torch = torch_cuda
+    from paged_kv_cache_block_amd import binding
+    from paged_kv_cache_block_amd.step import TORCH_DTYPE, to_numpy, to_torch
+    from workloads import round_to_dtype
+    rng = np.random.default_rng(5000 + seed)
+    dtype = str(rng.choice(["f16", "bf16", "f32"]))
+    bs = int(rng.choice([4, 8, 16, 32, 64] + ([128] if dtype != "f32" else [])))
+    h = int(rng.choice([1, 2, 3, 8]))
+    d = int(rng.choice([64, 128]))
+    nb = int(rng.integers(8, 96))
+    k = round_to_dtype(rng.standard_normal((nb, h, bs, d), dtype=np.float32), dtype)
+    v = round_to_dtype(rng.standard_normal((nb, h, d, bs), dtype=np.float32), dtype)
+    perm = rng.permutation(nb)
+    m = int(rng.integers(0, nb // 2 + 1))
+    pairs = np.stack([perm[:m], perm[m:2 * m]], 1).astype(np.int32)
+    t = int(rng.integers(1, min(nb * bs, 700) + 1))
+    slots = rng.choice(nb * bs, size=t, replace=False).astype(np.int64)
+    slots[rng.random(t) < 0.1] = -1
+    kn = round_to_dtype(rng.standard_normal((t, h, d), dtype=np.float32), dtype)
+    vn = round_to_dtype(rng.standard_normal((t, h, d), dtype=np.float32), dtype)
+    say("random copy+write", seed, dtype, "bs", bs, "H", h, "D", d, "blocks", nb, "pairs", m, "tokens", t)
+    kc, vc = to_torch(k, dtype, "cuda"), to_torch(v, dtype, "cuda")
+    binding.pa_copy_blocks(kc, vc, torch.from_numpy(pairs).cuda())
+    binding.pa_write_kv(to_torch(kn, dtype, "cuda"), to_torch(vn, dtype, "cuda"),
+                        torch.from_numpy(slots).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    oracle.copy_blocks(k, v, pairs)
+    oracle.write_kv(k, v, kn, vn, slots)
+    assert np.array_equal(bits(to_numpy(kc, dtype)), bits(k))
+    assert np.array_equal(bits(to_numpy(vc, dtype)), bits(v))
+
+
 @pytest.mark.parametrize("mode", ["default", "split64", "rows", "stream", "tile128", "tile256",
                                   "psplit128", "psplit128w", "nopsplit"])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
