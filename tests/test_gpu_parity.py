@@ -508,6 +508,26 @@ def test_chunk_recompute_shape(torch_cuda, psplit):
         compare(db.out_numpy(), want, w.dtype, what=f"chunks split {psplit} rows {rows}")
 
 
+def test_long_contexts(torch_cuda):
+    """A decode row after 100K cached tokens and a 16-token chunk after 60K
+    (hundreds of block-table windows, up to 1563 key splits of one row merged
+    by the combine), beside a short decode, against the oracle: automatic
+    splits, 64-key splits, and the vector-ALU row path."""
+    from paged_kv_cache_block_amd import binding
+    seqs = [(100_000, 1, 1), (60_000, 16, 2), (5, 1, 1)]
+    nblocks = sum(-(-(h + n) // 16) for h, n, _ in seqs) + 64
+    w = build_batch("long contexts bf16", "bf16", 16, 2, 128, 16, nblocks, seqs, 31)
+    k, v = oracle_step(w)
+    want = oracle.attention(w.q, k, v, w.block_tables, w.context_lens, w.query_start_loc,
+                            w.num_kv_heads, w.dtype, w.scale)
+    for mode, opt in [("default", None), ("split64", binding.options(64, 64)),
+                      ("rows", binding.options(0, 0, binding.PA_FLAG_VECTOR_ALU))]:
+        say("long contexts", mode)
+        db = run_gpu(w, opt)
+        compare(db.out_numpy(), want, w.dtype, what=f"long contexts [{mode}]")
+        del db
+
+
 @pytest.mark.parametrize("nseq", [37, 300])
 @pytest.mark.parametrize("psplit", [0, 128])
 def test_many_multi_token_sequences(torch_cuda, nseq, psplit):
