@@ -6,14 +6,19 @@ HBM: copy-on-write block copies, the slot-mapping write of the new tokens,
 and causal paged attention of every query row (plan, multi-token MFMA
 kernel, decode kernel, split combine).  The write and attention go through
 one pa_write_kv_attention call (the write shares the planner's launch);
-``--separate-write`` times pa_write_kv + pa_attention.  The default workload is the
-64-sequence fp16 decode batch at 40 heads x 128 (block size 16, contexts
-uniform in 128..2048); ``--config`` picks another named workload.
+``--separate-write`` times pa_write_kv + pa_attention.  The default workload is
+the long mixed bf16 batch (16 requests of 512 new tokens over 3000..4096
+cached tokens, beside 128 decodes over 1024..4096 tokens; 64 query / 8 KV
+heads of 128, block size 32), the largest named workload and the one with
+both a multi-token and a decode part; ``--config`` picks another.
 
 Prints one JSON line.  ``value`` is whole-step throughput in GB/s of
 algorithmic bytes; ``roofline`` rates the dominant kernel from its own
-per-launch HIP events; ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same batch.
+per-launch HIP events (the multi-token kernel against the bf16 MFMA peak, or
+the decode kernel against HBM), and ``roofline_decode`` /
+``roofline_multi_token`` rate the other attention kernel of a mixed batch the
+same way; ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same batch.
 """
 from __future__ import annotations
 
@@ -527,7 +532,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -667,36 +672,62 @@ def main(argv=None) -> int:
     value = model["step_bytes"] / (ms_step * 1e-3) / 1e9
     rows_kernel = ("decode_mfma_kernel" if w.dtype != "f32" and w.block_size in (16, 32)
                    else "row_attn_kernel")
-    if dominant == "rows":
-        achieved = model["rows_bytes"] / (dom_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": rows_kernel, "algorithmic_bytes": model["rows_bytes"],
-                "avg_ms": round(dom_ms, 5)}
-        if model["rows_unique_bytes"] < model["rows_bytes"]:
-            # Blocks shared by several rows: the same rate over bytes counted once.
-            roof["unique_bytes"] = model["rows_unique_bytes"]
-            roof["achieved_unique"] = round(model["rows_unique_bytes"] / (dom_ms * 1e-3) / 1e9, 1)
-    else:
-        achieved = model["tile_flops"] / (dom_ms * 1e-3) / 1e12
-        peak = MFMA_PEAK_TFLOPS[w.dtype]
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": "tile_attn_kernel",
-                "algorithmic_flops": model["tile_flops"], "avg_ms": round(dom_ms, 5)}
-    from paged_kv_cache_block_amd.profiling import traffic_record_for
-    rec = (traffic_record_for(roof["kernel"], args.config)
-           if args.split == 0 and args.tile_rows == 0 and args.prefill_split == 0
-           and not flags & binding.PA_FLAG_NO_PREFILL_SPLIT else None)
-    if rec is not None:
-        roof["traffic"] = rec["fetch_bytes"] + rec["write_bytes"]
-        roof["traffic_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                "scaled by pa_copy_blocks over a known byte count")
+    from paged_kv_cache_block_amd.profiling import counter_record_for, traffic_record_for
+    stored_ok = (args.split == 0 and args.tile_rows == 0 and args.prefill_split == 0
+                 and not flags & binding.PA_FLAG_NO_PREFILL_SPLIT)
+
+    def roof_block(which, ms):
+        """Roofline of one attention kernel from its mean launch time."""
+        if which == "rows":
+            achieved = model["rows_bytes"] / (ms * 1e-3) / 1e9
+            r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                 "kernel": rows_kernel, "algorithmic_bytes": model["rows_bytes"],
+                 "avg_ms": round(ms, 5)}
+            if model["rows_unique_bytes"] < model["rows_bytes"]:
+                # Blocks shared by several rows (reference counts): the bytes
+                # that must cross from HBM count each cached slot once.  The
+                # fraction of peak is stated on those, so it cannot pass 1.
+                au = model["rows_unique_bytes"] / (ms * 1e-3) / 1e9
+                r.update({"unique_bytes": model["rows_unique_bytes"], "achieved_unique": round(au, 1),
+                          "frac": round(au / HBM_PEAK_GBS, 4),
+                          "frac_logical": round(achieved / HBM_PEAK_GBS, 4),
+                          "frac_note": "frac on unique bytes (each cached slot once); "
+                                       "frac_logical counts each row's context once per KV head"})
+        else:
+            achieved = model["tile_flops"] / (ms * 1e-3) / 1e12
+            peak = MFMA_PEAK_TFLOPS[w.dtype]
+            r = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                 "frac": round(achieved / peak, 4), "traffic": None, "kernel": "tile_attn_kernel",
+                 "algorithmic_flops": model["tile_flops"], "avg_ms": round(ms, 5)}
+        rec = traffic_record_for(r["kernel"], args.config) if stored_ok else None
+        if rec is not None:
+            r["traffic"] = rec["fetch_bytes"] + rec["write_bytes"]
+            r["traffic_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                 "scaled by pa_copy_blocks over a known byte count")
+        if which == "tile":
+            mrec = counter_record_for("mfma-record", "tile_attn_kernel", args.config) if stored_ok else None
+            if mrec is not None:
+                r["mfma_busy"] = mrec["mfma_busy_frac"]
+                r["mfma_busy_note"] = ("SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE per XCD), "
+                                       "rocprofv3 --pmc of the same command")
+        return r
+
+    roof = roof_block(dominant, dom_ms)
+    others = {}
+    for name, _ in kernels:
+        if name != dominant:
+            others["roofline_decode" if name == "rows" else "roofline_multi_token"] = \
+                roof_block(name, per_kernel[name])
     if dom_cold_ms is not None:
         unit_work = model["rows_bytes"] if dominant == "rows" else model["tile_flops"]
         roof["cold_cache"] = {
             "avg_ms": round(dom_cold_ms, 5),
             "achieved": round(unit_work / (dom_cold_ms * 1e-3) / (1e9 if dominant == "rows" else 1e12), 1),
             "note": "the same kernel with a 512 MiB write before every step (L2 and MALL flushed)"}
+        if dominant == "rows" and "unique_bytes" in roof:
+            roof["cold_cache"]["achieved_unique"] = round(
+                model["rows_unique_bytes"] / (dom_cold_ms * 1e-3) / 1e9, 1)
     extra = {}
     if "tile" in per_kernel:
         extra["multi_token_tflops"] = round(model["tile_flops"] / (per_kernel["tile"] * 1e-3) / 1e12, 1)
@@ -722,6 +753,7 @@ def main(argv=None) -> int:
                             else "pa_copy_blocks, pa_write_kv_attention"),
                    "step_bytes": model["step_bytes"], "multi_token_flops": model["tile_flops"]},
         "roofline": roof,
+        **others,
         "kernels_ms": {k2: round(v, 5) for k2, v in per_kernel.items()},
         "derived": extra,
         "cpu_baseline": cpu,

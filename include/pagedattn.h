@@ -226,6 +226,38 @@ size_t pa_attention_workspace_size(const pa_cache_desc* c, int32_t num_q_heads,
                                    int32_t max_context_len, const pa_options* opt);
 
 /*
+ * pa_attention_plan -- the plan pa_attention would make for a batch, on the
+ * host only (no GPU work, no device memory touched).
+ *
+ * Pensieve page (实验结果, multi-token kernel): the per-request auxiliary data
+ * that lets the paged kernel run like a contiguous one is derived on the CPU
+ * side; this call exposes what the library derives from the host mirrors.
+ *
+ *  Arguments as for pa_attention; workspace_bytes is the workspace the call
+ *  would be given (the automatic multi-token split is lengthened until its
+ *  partial states fit it).  info (may be NULL) receives the work counts, the
+ *  chosen split lengths and tile rows, and the workspace bytes the plan
+ *  occupies.  Returns PA_OK when the plan fits workspace_bytes,
+ *  PA_ERR_WORKSPACE when it does not (info is still filled), or the argument
+ *  error pa_attention would return.
+ */
+typedef struct {
+  int64_t row_items;             /* single-row work items (row, key split) */
+  int64_t tile_items;            /* multi-token work items (row tile, key split) */
+  int64_t combine_items;         /* rows whose key splits are merged */
+  int64_t partial_slots;         /* partial softmax states of split rows */
+  int32_t decode_split_tokens;   /* keys per split of a single row */
+  int32_t prefill_split_tokens;  /* keys per split of a multi-token context, 0 = none */
+  int32_t prefill_tile_rows;     /* (token, head) rows per multi-token work item */
+  int32_t reserved;              /* 0 */
+  size_t workspace_bytes;        /* workspace the plan occupies */
+} pa_plan_info;
+pa_status pa_attention_plan(const pa_cache_desc* c, int32_t num_q_heads,
+                            int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_q,
+                            const int32_t* context_lens_host, const int32_t* query_start_loc_host,
+                            size_t workspace_bytes, const pa_options* opt, pa_plan_info* info);
+
+/*
  * pa_attention -- causal attention of a ragged batch over the paged cache.
  *
  * Pensieve page (LLM与注意力机制): A = Q K^T * scale, O = softmax(A) V per
@@ -259,12 +291,16 @@ size_t pa_attention_workspace_size(const pa_cache_desc* c, int32_t num_q_heads,
  *                  contents; used on the host for validation and launch
  *                  sizing.
  *  scale           multiplies q.k (usually 1/sqrt(head_dim)).
- *  workspace       device, at least pa_attention_workspace_size(...) bytes,
- *                  256-byte aligned; contents on entry are ignored.
+ *  workspace       device, 256-byte aligned, at least the bytes the batch's
+ *                  plan occupies (pa_attention_plan); a workspace of
+ *                  pa_attention_workspace_size(...) bytes always suffices.
+ *                  Contents on entry are ignored; on return it holds the
+ *                  plan and its status (pa_attention_check).
  *  opt             NULL or tuning options (same as given to the size query).
  *  Errors: PA_ERR_INVALID_ARG if num_q_heads % num_kv_heads != 0, n_s > L_s,
  *  qsl is not non-decreasing from 0 to total_q, or L_s > max_blocks_per_seq*bs;
- *  PA_ERR_WORKSPACE if the workspace is too small.
+ *  PA_ERR_WORKSPACE if the workspace is too small.  Device data that
+ *  disagree with the host mirrors are reported by pa_attention_check.
  *  Sub-requests (two query ranges over one context) are expressed by giving
  *  two sequences the same block-table row with different context_lens and
  *  query ranges.
@@ -310,6 +346,22 @@ pa_status pa_write_kv_attention(void* out, const void* q, const void* k_new, con
                                 const int32_t* query_start_loc_host, float scale,
                                 void* workspace, size_t workspace_bytes, const pa_options* opt,
                                 hipStream_t stream);
+
+/*
+ * pa_attention_check -- wait for `stream`, then report whether the last
+ * pa_attention / pa_write_kv_attention call that used `workspace` ran every
+ * work item it was sized for.
+ *
+ * The grids of a call are sized on the host from the host mirrors, and the
+ * device plans from context_lens / query_start_loc.  If the two disagree, or
+ * a kernel meets an index outside the batch or the workspace, work is skipped
+ * (never read or written out of bounds) and the call's first kernel records
+ * it in the workspace.  PA_OK: every item ran.  PA_ERR_BOUNDS: the
+ * descriptions differed or work was skipped; the output is not valid.
+ * PA_ERR_HIP: the stream or the read failed.  Under PA_VALIDATE=1 every
+ * attention call ends with this check (and so synchronizes).
+ */
+pa_status pa_attention_check(const void* workspace, hipStream_t stream);
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* pa_last_error(void);

@@ -9,6 +9,7 @@ raises ``ImportError`` when it has not been built.  Build with
 
 _API = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks",
         "pa_attention", "pa_write_kv_attention", "pa_attention_workspace_size",
+        "pa_attention_plan", "pa_attention_check",
         "cache_desc", "options", "version", "PagedAttnError", "LIB_PATH")
 
 

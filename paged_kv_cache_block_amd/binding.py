@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -19,7 +20,8 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "P
           -4: "PA_ERR_HIP", -5: "PA_ERR_BOUNDS"}
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 SYMBOLS = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks",
-           "pa_attention_workspace_size", "pa_attention", "pa_last_error", "pa_version")
+           "pa_attention_workspace_size", "pa_attention_plan", "pa_attention",
+           "pa_write_kv_attention", "pa_attention_check", "pa_last_error", "pa_version")
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 MAX_LAYERS = 128
 
@@ -35,6 +37,14 @@ class PaOptions(ctypes.Structure):
                 ("flags", ctypes.c_int32), ("timed_kernel", ctypes.c_int32),
                 ("timing_start", ctypes.c_void_p), ("timing_end", ctypes.c_void_p),
                 ("prefill_tile_rows", ctypes.c_int32)]
+
+
+class PaPlanInfo(ctypes.Structure):
+    _fields_ = [("row_items", ctypes.c_int64), ("tile_items", ctypes.c_int64),
+                ("combine_items", ctypes.c_int64), ("partial_slots", ctypes.c_int64),
+                ("decode_split_tokens", ctypes.c_int32), ("prefill_split_tokens", ctypes.c_int32),
+                ("prefill_tile_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 PA_TIME_NONE, PA_TIME_TILE, PA_TIME_ROWS, PA_TIME_COMBINE = 0, 1, 2, 3
@@ -72,6 +82,11 @@ def _load() -> ctypes.CDLL:
                                           i32p, i32p, i32, i32, i32p, i32p, ctypes.c_float, vp,
                                           ctypes.c_size_t, opt_p, vp]
     lib.pa_write_kv_attention.restype = ctypes.c_int
+    lib.pa_attention_plan.argtypes = [desc_p, i32, i32, i32, i32, i32p, i32p, ctypes.c_size_t, opt_p,
+                                      ctypes.POINTER(PaPlanInfo)]
+    lib.pa_attention_plan.restype = ctypes.c_int
+    lib.pa_attention_check.argtypes = [vp, vp]
+    lib.pa_attention_check.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
@@ -97,6 +112,31 @@ def _ptr(t) -> int | None:
     return None if t is None else int(t.data_ptr())
 
 
+def _on_device(dev: torch.device, **tensors) -> None:
+    """Every named tensor must live on ``dev`` (the pools' GPU): a host
+    pointer handed to a kernel would fault the GPU."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.device != dev:
+            where = t.device if isinstance(t, torch.Tensor) else type(t).__name__
+            raise ValueError(f"{name} must be a tensor on {dev}, got {where}")
+
+
+def _on_host(**tensors) -> None:
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor) or t.device.type != "cpu":
+            where = t.device if isinstance(t, torch.Tensor) else type(t).__name__
+            raise ValueError(f"{name} must be a CPU tensor, got {where}")
+
+
+def _pairs(block_pairs) -> int:
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2 \
+            or not block_pairs.is_contiguous():
+        raise ValueError("block_pairs must be a contiguous int32 [n][2] tensor")
+    return int(block_pairs.shape[0])
+
+
 def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> PaCacheDesc:
     """Descriptor of a pool pair: K [NB][H][bs][D], V [NB][H][D][bs]."""
     if k_cache.dim() != 4 or v_cache.dim() != 4:
@@ -108,6 +148,8 @@ def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> PaCacheDesc:
         raise ValueError("pools must share a dtype among float32, float16, bfloat16")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("pools must be contiguous")
+    if k_cache.device.type == "cuda" and v_cache.device != k_cache.device:
+        raise ValueError("k_cache and v_cache must be on the same GPU")
     return PaCacheDesc(nb, bs, h, d, TORCH_TO_PA[k_cache.dtype])
 
 
@@ -133,8 +175,11 @@ def pa_write_kv(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> No
         if tuple(x.shape) != (t, desc.num_kv_heads, desc.head_dim) or x.dtype != k_cache.dtype \
                 or not x.is_contiguous():
             raise ValueError("k_new/v_new must be contiguous [T][H_kv][D] in the pool dtype")
-    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (t,):
-        raise ValueError("slot_mapping must be int64 [T]")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (t,) \
+            or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int64 [T] tensor")
+    _on_device(k_cache.device, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
+               slot_mapping=slot_mapping)
     _check(LIB.pa_write_kv(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), t, _ptr(k_cache),
                            _ptr(v_cache), ctypes.byref(desc), _stream(stream)))
 
@@ -148,14 +193,19 @@ def pa_copy_blocks_layers(k_caches, v_caches, block_pairs, stream=None) -> None:
         if tuple(k.shape) != tuple(k_caches[0].shape) or k.dtype != k_caches[0].dtype or \
                 tuple(v.shape) != tuple(v_caches[0].shape):
             raise ValueError("every layer's pools must have the same shape and dtype")
-    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
-        raise ValueError("block_pairs must be int32 [n][2]")
+    npairs = _pairs(block_pairs)
+    dev = k_caches[0].device
+    for l, (k, v) in enumerate(zip(k_caches, v_caches)):
+        _on_device(dev, **{f"k_caches[{l}]": k, f"v_caches[{l}]": v})
+        if not (k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("every layer's pools must be contiguous")
+    _on_device(dev, block_pairs=block_pairs)
     n = len(k_caches)
     kp = (ctypes.c_void_p * n)(*[_ptr(k) for k in k_caches])
     vp_ = (ctypes.c_void_p * n)(*[_ptr(v) for v in v_caches])
     _check(LIB.pa_copy_blocks_layers(ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp_, ctypes.c_void_p),
-                                     n, ctypes.byref(desc), _ptr(block_pairs.contiguous()),
-                                     int(block_pairs.shape[0]), _stream(stream)))
+                                     n, ctypes.byref(desc), _ptr(block_pairs), npairs,
+                                     _stream(stream)))
 
 
 def pa_swap_blocks(dev_k, dev_v, host_k, host_v, block_pairs, direction: int, stream=None) -> None:
@@ -171,22 +221,20 @@ def pa_swap_blocks(dev_k, dev_v, host_k, host_v, block_pairs, direction: int, st
         raise ValueError("host pools must match the device pools' block shape and dtype")
     if not (host_k.is_contiguous() and host_v.is_contiguous()):
         raise ValueError("host pools must be contiguous")
-    if block_pairs.device.type != "cpu" or block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 \
-            or block_pairs.shape[1] != 2:
-        raise ValueError("block_pairs must be an int32 CPU tensor [n][2]")
-    pairs = block_pairs.contiguous()
+    _on_device(dev_k.device, dev_k=dev_k, dev_v=dev_v)
+    _on_host(block_pairs=block_pairs)
+    npairs = _pairs(block_pairs)
     _check(LIB.pa_swap_blocks(_ptr(dev_k), _ptr(dev_v), ctypes.byref(desc), _ptr(host_k), _ptr(host_v),
-                              int(host_k.shape[0]), _ptr(pairs), int(pairs.shape[0]), int(direction),
+                              int(host_k.shape[0]), _ptr(block_pairs), npairs, int(direction),
                               _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
     desc = cache_desc(k_cache, v_cache)
-    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
-        raise ValueError("block_pairs must be int32 [n][2]")
+    npairs = _pairs(block_pairs)
+    _on_device(k_cache.device, k_cache=k_cache, v_cache=v_cache, block_pairs=block_pairs)
     _check(LIB.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
-                              _ptr(block_pairs.contiguous()), int(block_pairs.shape[0]),
-                              _stream(stream)))
+                              _ptr(block_pairs), npairs, _stream(stream)))
 
 
 def pa_attention_workspace_size(desc: PaCacheDesc, num_q_heads: int, num_seqs: int, total_q: int,
@@ -196,8 +244,33 @@ def pa_attention_workspace_size(desc: PaCacheDesc, num_q_heads: int, num_seqs: i
                                                ctypes.byref(opt) if opt is not None else None))
 
 
-def _attention_args(out, q, k_cache, block_tables, context_lens, query_start_loc,
-                    context_lens_host, query_start_loc_host):
+def pa_attention_plan(desc: PaCacheDesc, num_q_heads: int, max_blocks_per_seq: int,
+                      context_lens_host, query_start_loc_host, workspace_bytes: int,
+                      opt: PaOptions | None = None) -> tuple[int, PaPlanInfo]:
+    """Host-only: the plan ``pa_attention`` would make for this batch given a
+    workspace of ``workspace_bytes``.  Returns ``(status, info)``; status 0
+    when the plan fits, -3 when it does not (``info`` is filled either way)."""
+    lens = np.ascontiguousarray(context_lens_host, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc_host, dtype=np.int32)
+    if qsl.shape[0] != lens.shape[0] + 1:
+        raise ValueError("query_start_loc must have one more entry than context_lens")
+    info = PaPlanInfo()
+    st = LIB.pa_attention_plan(ctypes.byref(desc), num_q_heads, max_blocks_per_seq, lens.shape[0],
+                               int(qsl[-1]) if qsl.size else 0, lens.ctypes.data, qsl.ctypes.data,
+                               int(workspace_bytes), ctypes.byref(opt) if opt is not None else None,
+                               ctypes.byref(info))
+    return int(st), info
+
+
+def pa_attention_check(workspace, stream=None) -> None:
+    """Wait for the stream; raise PagedAttnError if the last attention call
+    that used ``workspace`` skipped work (device batch != host mirrors)."""
+    _on_device(workspace.device, workspace=workspace)
+    _check(LIB.pa_attention_check(_ptr(workspace), _stream(stream)))
+
+
+def _attention_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                    context_lens_host, query_start_loc_host, workspace):
     tq, hq, d = q.shape
     if tuple(out.shape) != (tq, hq, d) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
         raise ValueError("q/out must be [T_q][H_q][D] in the pool dtype")
@@ -212,6 +285,11 @@ def _attention_args(out, q, k_cache, block_tables, context_lens, query_start_loc
             raise ValueError("host mirrors must be contiguous int32 CPU tensors")
     if block_tables.dim() != 2 or block_tables.shape[0] != s or query_start_loc.shape[0] != s + 1:
         raise ValueError("block_tables [S][max_blocks] and query_start_loc [S+1] expected")
+    if context_lens_host.shape[0] != s or query_start_loc_host.shape[0] != s + 1:
+        raise ValueError("host mirrors must match context_lens [S] and query_start_loc [S+1]")
+    _on_device(k_cache.device, k_cache=k_cache, v_cache=v_cache, out=out, q=q,
+               block_tables=block_tables, context_lens=context_lens,
+               query_start_loc=query_start_loc, workspace=workspace)
     return tq, hq, s
 
 
@@ -224,8 +302,9 @@ def pa_attention(out, q, k_cache, v_cache, block_tables, context_lens, query_sta
     tensors with the same contents as their device counterparts.
     """
     desc = cache_desc(k_cache, v_cache)
-    tq, hq, s = _attention_args(out, q, k_cache, block_tables, context_lens, query_start_loc,
-                                context_lens_host, query_start_loc_host)
+    tq, hq, s = _attention_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                query_start_loc, context_lens_host, query_start_loc_host,
+                                workspace)
     _check(LIB.pa_attention(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
                             hq, _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
                             _ptr(query_start_loc), s, tq, _ptr(context_lens_host),
@@ -243,8 +322,9 @@ def pa_write_kv_attention(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, 
     by ``pa_attention``, in one call (the write shares the planner's
     launch)."""
     desc = cache_desc(k_cache, v_cache)
-    tq, hq, s = _attention_args(out, q, k_cache, block_tables, context_lens, query_start_loc,
-                                context_lens_host, query_start_loc_host)
+    tq, hq, s = _attention_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                query_start_loc, context_lens_host, query_start_loc_host,
+                                workspace)
     if tuple(k_new.shape) != (tq, desc.num_kv_heads, desc.head_dim) or k_new.shape != v_new.shape:
         raise ValueError("k_new/v_new must be [T_q][H_kv][D]")
     if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
@@ -254,6 +334,7 @@ def pa_write_kv_attention(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, 
     if (slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous()
             or slot_mapping.numel() != tq):
         raise ValueError("slot_mapping must be a contiguous int64 [T_q] tensor")
+    _on_device(k_cache.device, k_new=k_new, v_new=v_new, slot_mapping=slot_mapping)
     _check(LIB.pa_write_kv_attention(
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
         _ptr(v_cache), ctypes.byref(desc), hq, _ptr(block_tables), int(block_tables.shape[1]),

@@ -3,10 +3,8 @@
     python -m paged_kv_cache_block_amd.build [-v] [-j N]
 
 Each HIP source compiles to an object under ``_build/`` (in parallel), and
-the objects link into ``paged_kv_cache_block_amd/libpagedattn.so``.  The
-hardware-ceiling probes (``hw_probes.hip``) build into the program
-``paged_kv_cache_block_amd/hw_probes``.  Packed fp32 vector instructions are
-disabled for device code.
+the objects link into ``paged_kv_cache_block_amd/libpagedattn.so``.  Packed
+fp32 vector instructions are disabled for device code.
 """
 from __future__ import annotations
 
@@ -24,8 +22,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
-PROBES_SRC = os.path.join(PKG, "hw_probes.hip")
-PROBES = os.path.join(PKG, "hw_probes")      # hardware-ceiling probes (a program, not the library)
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -59,26 +55,12 @@ def _compile(src: str, verbose: bool) -> tuple[str, float, str]:
     return obj, time.time() - t, log
 
 
-def _build_probes() -> str:
-    tmp = PROBES + ".tmp"
-    cmd = [hipcc(), PROBES_SRC, "-o", tmp, "-O3", "-std=c++17", f"--offload-arch={ARCH}"] + DEVICE_FLAGS
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        noise = "'-packed-fp32-ops' is not a recognized feature"
-        log = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-        raise RuntimeError(f"hipcc failed for hw_probes.hip:\n{log}")
-    os.replace(tmp, PROBES)
-    return PROBES
-
-
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs) + 1, os.cpu_count() or 4, 16)
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        probes = ex.submit(_build_probes)
         results = list(ex.map(lambda s: _compile(s, verbose), srcs))
-        probes.result()
     objs = [r[0] for r in results]
     if verbose:
         for s, (_, dt, _) in zip(srcs, results):

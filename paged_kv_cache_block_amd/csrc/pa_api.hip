@@ -194,6 +194,42 @@ WorkspaceLayout make_layout(const PoolArgs& p, int hq, int num_seqs, int total_q
   return w;
 }
 
+// The layout of one call's plan, sized by its exact work counts (never more
+// than make_layout's bound for a batch within that bound's arguments).
+WorkspaceLayout exact_layout(const PoolArgs& p, int hq, int64_t rows, int64_t tiles, int64_t combs,
+                             int64_t partials) {
+  WorkspaceLayout w{};
+  w.cap_rows = rows;
+  w.cap_tiles = tiles;
+  w.cap_combs = combs;
+  w.cap_partials = partials;
+  size_t off = 0;
+  w.counts = off; off = align256(off + sizeof(PlanCounts));
+  w.rows = off;   off = align256(off + sizeof(RowItem) * (size_t)rows);
+  w.tiles = off;  off = align256(off + sizeof(TileItem) * (size_t)tiles);
+  w.combs = off;  off = align256(off + sizeof(CombItem) * (size_t)combs);
+  w.part_ml = off; off = align256(off + 8ull * (size_t)partials * hq);
+  w.part_o = off;  off = align256(off + 4ull * (size_t)partials * hq * p.head_dim);
+  w.total = off;
+  return w;
+}
+
+// Everything the host decides about one attention call: checked shapes, the
+// split and tile choices, the exact work counts and the workspace layout.
+struct CallPlan {
+  PoolArgs p;
+  int group = 0, max_len = 0, split = 0, tile_rows = kTileRows, psplit = 0;
+  bool va = false, rows_on_mfma = false;
+  int64_t n_rows = 0, n_tiles = 0, n_combs = 0, n_partials = 0;
+  WorkspaceLayout lay{};
+};
+
+pa_status plan_call(const pa_cache_desc* c, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                    int32_t num_seqs, int32_t total_q, const int32_t* context_lens_host,
+                    const int32_t* query_start_loc_host, size_t workspace_bytes,
+                    const pa_options* opt, CallPlan* cp);
+pa_status read_status(const void* workspace, hipStream_t stream);
+
 // PA_VALIDATE checks of a slot mapping: every slot inside the pool, no slot
 // twice.  The mapping is left in `slots`.
 pa_status check_slots(std::vector<int64_t>& slots, const int64_t* slot_mapping, int num_tokens,
@@ -408,6 +444,32 @@ size_t pa_attention_workspace_size(const pa_cache_desc* c, int32_t num_q_heads, 
   return make_layout(p, num_q_heads, num_seqs, total_q, max_context_len, opt).total;
 }
 
+pa_status pa_attention_plan(const pa_cache_desc* c, int32_t num_q_heads,
+                            int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_q,
+                            const int32_t* context_lens_host, const int32_t* query_start_loc_host,
+                            size_t workspace_bytes, const pa_options* opt, pa_plan_info* info) {
+  CallPlan cp;
+  const pa_status st = plan_call(c, num_q_heads, max_blocks_per_seq, num_seqs, total_q,
+                                 context_lens_host, query_start_loc_host, workspace_bytes, opt, &cp);
+  if (info && (st == PA_OK || st == PA_ERR_WORKSPACE)) {
+    info->row_items = cp.n_rows;
+    info->tile_items = cp.n_tiles;
+    info->combine_items = cp.n_combs;
+    info->partial_slots = cp.n_partials;
+    info->decode_split_tokens = cp.split;
+    info->prefill_split_tokens = cp.psplit;
+    info->prefill_tile_rows = cp.tile_rows;
+    info->reserved = 0;
+    info->workspace_bytes = cp.lay.total;
+  }
+  return st;
+}
+
+pa_status pa_attention_check(const void* workspace, hipStream_t stream) {
+  if (!workspace) return fail(PA_ERR_INVALID_ARG, "workspace is null");
+  return read_status(workspace, stream);
+}
+
 pa_status pa_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const pa_cache_desc* c, int32_t num_q_heads, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -443,20 +505,18 @@ pa_status pa_write_kv_attention(void* out, const void* q, const void* k_new, con
 
 namespace {
 
-pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
-                         const pa_cache_desc* c, int32_t num_q_heads, const int32_t* block_tables,
-                         int32_t max_blocks_per_seq, const int32_t* context_lens,
-                         const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
-                         const int32_t* context_lens_host, const int32_t* query_start_loc_host,
-                         float scale, void* workspace, size_t workspace_bytes,
-                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream) {
-  PoolArgs p;
+pa_status plan_call(const pa_cache_desc* c, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                    int32_t num_seqs, int32_t total_q, const int32_t* context_lens_host,
+                    const int32_t* query_start_loc_host, size_t workspace_bytes,
+                    const pa_options* opt, CallPlan* cp) {
+  PoolArgs& p = cp->p;
   pa_status st = check_desc(c, &p);
   if (st != PA_OK) return st;
   if (num_q_heads <= 0 || num_q_heads % p.num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                 num_q_heads, p.num_kv_heads);
   const int group = num_q_heads / p.num_kv_heads;
+  cp->group = group;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %d not supported", group);
   if (num_seqs < 0 || total_q < 0) return fail(PA_ERR_INVALID_ARG, "negative num_seqs or total_q");
@@ -488,9 +548,110 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
       return fail(PA_ERR_INVALID_ARG, "sequence %d context %d exceeds its block table", s, L);
     max_len = std::max(max_len, L);
   }
+  cp->max_len = max_len;
   if ((num_seqs > 0 && query_start_loc_host[num_seqs] != total_q) || (num_seqs == 0 && total_q != 0))
     return fail(PA_ERR_INVALID_ARG, "query_start_loc[num_seqs] != total_q");
+
+  // Work counts: the same functions the plan kernel runs on the device.
+  const bool va = vector_all(p, opt);
+  cp->va = va;
+  int64_t total_keys = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
+    const int L = context_lens_host[s];
+    const SeqWork w = seq_work(n, va ? 1 : 0, group, kTileRows);
+    for (int i = w.row_first; i < w.row_first + w.rows; ++i) total_keys += L - n + i + 1;
+  }
+  const int split = choose_split(opt, total_keys, p.num_kv_heads, group);
+  cp->split = split;
+  // Wide (256-row) multi-token work items when there are enough of them.
+  int tile_rows = kTileRows;
+  if (opt && opt->prefill_tile_rows) {
+    tile_rows = opt->prefill_tile_rows;
+  } else if (!va) {
+    int64_t wide = 0;
+    for (int s = 0; s < num_seqs; ++s)
+      wide += seq_work(query_start_loc_host[s + 1] - query_start_loc_host[s], 0, group,
+                       kTileRowsWide).tiles;
+    if (wide * p.num_kv_heads >= kWideTileMinGroups) tile_rows = kTileRowsWide;
+  }
+  cp->tile_rows = tile_rows;
+  int psplit = va ? 0
+               : auto_prefill_split(opt)
+                   ? choose_prefill_split(context_lens_host, query_start_loc_host, num_seqs,
+                                          group, tile_rows, p.num_kv_heads)
+                   : prefill_split(opt);
+  auto count = [&]() {
+    cp->n_rows = cp->n_tiles = cp->n_combs = cp->n_partials = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
+      const int L = context_lens_host[s];
+      const SeqWork w = seq_work(n, va ? 1 : 0, group, tile_rows);
+      for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
+        const int ns = row_splits(L - n + i + 1, split);
+        cp->n_rows += ns;
+        if (ns > 1) {
+          cp->n_combs += 1;
+          cp->n_partials += ns;
+        }
+      }
+      const TileWork tw = tile_work(n, L, group, tile_rows, w.tiles, psplit);
+      cp->n_tiles += tw.items;
+      cp->n_combs += tw.combs;
+      cp->n_partials += tw.slots;
+    }
+    cp->lay = exact_layout(p, num_q_heads, cp->n_rows, cp->n_tiles, cp->n_combs, cp->n_partials);
+    return cp->lay.total <= workspace_bytes;
+  };
+  bool fits = count();
+  // An automatic multi-token split whose partial states do not fit the
+  // workspace is lengthened until they do (pa_attention_workspace_size
+  // reserves room for kMinAutoPrefillSplit-key splits).
+  while (!fits && psplit > 0 && auto_prefill_split(opt)) {
+    const int longer = (psplit + psplit / 4 + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum *
+                       kPrefillSplitQuantum;
+    psplit = psplit >= max_len ? 0 : std::max(longer, psplit + kPrefillSplitQuantum);
+    fits = count();
+  }
+  cp->psplit = psplit;
+  if (cp->n_rows > 0x7fffffff || cp->n_tiles > 0x7fffffff || cp->n_partials > 0x7fffffff)
+    return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
+  cp->rows_on_mfma = !va && decode_mfma_supported(p, group);
+  if (cp->n_rows > 0 && !cp->rows_on_mfma && p.block_size > 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d needs the fp16/bf16 MFMA kernels", p.block_size);
+  if (!fits)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                cp->lay.total);
+  return PA_OK;
+}
+
+// Status of the last call that used `workspace`, once `stream` is idle.
+pa_status read_status(const void* workspace, hipStream_t stream) {
+  PlanCounts pc{};
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(&pc, workspace, sizeof pc, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the plan status");
+  if (pc.mismatch)
+    return fail(PA_ERR_BOUNDS, "context_lens / query_start_loc on the device differ from the host mirrors");
+  if (pc.dropped)
+    return fail(PA_ERR_BOUNDS, "work items were skipped: an index left the batch or the workspace");
+  return PA_OK;
+}
+
+pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
+                         const pa_cache_desc* c, int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
+                         const int32_t* context_lens_host, const int32_t* query_start_loc_host,
+                         float scale, void* workspace, size_t workspace_bytes,
+                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream) {
+  CallPlan cp;
+  pa_status st = plan_call(c, num_q_heads, max_blocks_per_seq, num_seqs, total_q,
+                           context_lens_host, query_start_loc_host,
+                           workspace ? workspace_bytes : 0, opt, &cp);
+  if (st != PA_OK && !(st == PA_ERR_WORKSPACE && total_q == 0)) return st;
   if (total_q == 0) return PA_OK;
+  const PoolArgs& p = cp.p;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -501,10 +662,6 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
     return fail(PA_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
   if (fw && write_geom(total_q, p).chunks > 0x7fffffff)
     return fail(PA_ERR_UNSUPPORTED, "too many new tokens for one write (at most 2^31 - 1 16-byte chunks)");
-
-  const WorkspaceLayout lay = make_layout(p, num_q_heads, num_seqs, total_q, max_len, opt);
-  if (!workspace || workspace_bytes < lay.total)
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, lay.total);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
@@ -529,76 +686,12 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
     }
   }
 
-  // Launch sizes: the same counts the plan kernel derives on the device.
-  const bool va = vector_all(p, opt);
-  int64_t total_keys = 0;
-  for (int s = 0; s < num_seqs; ++s) {
-    const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
-    const int L = context_lens_host[s];
-    const SeqWork w = seq_work(n, va ? 1 : 0, group, kTileRows);
-    for (int i = w.row_first; i < w.row_first + w.rows; ++i) total_keys += L - n + i + 1;
-  }
-  const int split = choose_split(opt, total_keys, p.num_kv_heads, group);
-  // Wide (256-row) multi-token work items when there are enough of them.
-  int tile_rows = kTileRows;
-  if (opt && opt->prefill_tile_rows) {
-    tile_rows = opt->prefill_tile_rows;
-  } else if (!va) {
-    int64_t wide = 0;
-    for (int s = 0; s < num_seqs; ++s)
-      wide += seq_work(query_start_loc_host[s + 1] - query_start_loc_host[s], 0, group,
-                       kTileRowsWide).tiles;
-    if (wide * p.num_kv_heads >= kWideTileMinGroups) tile_rows = kTileRowsWide;
-  }
-  int psplit = va ? 0
-               : auto_prefill_split(opt)
-                   ? choose_prefill_split(context_lens_host, query_start_loc_host, num_seqs,
-                                          group, tile_rows, p.num_kv_heads)
-                   : prefill_split(opt);
-  int64_t n_rows = 0, n_tiles = 0, n_combs = 0, n_partials = 0;
-  auto count = [&]() {
-    n_rows = n_tiles = n_combs = n_partials = 0;
-    for (int s = 0; s < num_seqs; ++s) {
-      const int n = query_start_loc_host[s + 1] - query_start_loc_host[s];
-      const int L = context_lens_host[s];
-      const SeqWork w = seq_work(n, va ? 1 : 0, group, tile_rows);
-      for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
-        const int ns = row_splits(L - n + i + 1, split);
-        n_rows += ns;
-        if (ns > 1) {
-          n_combs += 1;
-          n_partials += ns;
-        }
-      }
-      const TileWork tw = tile_work(n, L, group, tile_rows, w.tiles, psplit);
-      n_tiles += tw.items;
-      n_combs += tw.combs;
-      n_partials += tw.slots;
-    }
-    return n_rows <= lay.cap_rows && n_tiles <= lay.cap_tiles && n_combs <= lay.cap_combs &&
-           n_partials <= lay.cap_partials;
-  };
-  bool fits = count();
-  // The workspace bound assumes automatic splits of at least
-  // kMinAutoPrefillSplit keys; a shorter (sparse-grid) split that does not
-  // fit is lengthened until it does.
-  while (!fits && psplit > 0 && auto_prefill_split(opt)) {
-    const int longer = (psplit + psplit / 4 + kPrefillSplitQuantum - 1) / kPrefillSplitQuantum *
-                       kPrefillSplitQuantum;
-    psplit = psplit >= max_len ? 0 : std::max(longer, psplit + kPrefillSplitQuantum);
-    fits = count();
-  }
-  if (!fits) return fail(PA_ERR_WORKSPACE, "plan exceeds workspace capacity");
-  if (n_rows > 0x7fffffff || n_tiles > 0x7fffffff)
-    return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
-  const bool rows_on_mfma = !va && decode_mfma_supported(p, group);
-  if (n_rows > 0 && !rows_on_mfma && p.block_size > 64)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d needs the fp16/bf16 MFMA kernels", p.block_size);
-
   // The plan, and with the fused write the new tokens' K/V stores too, in one
   // launch ahead of every kernel that reads the pools.
-  PlanParams pp{num_seqs, split, group, va ? 1 : 0, tile_rows, psplit,
-                lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials};
+  const WorkspaceLayout& lay = cp.lay;
+  PlanParams pp{num_seqs, cp.split, cp.group, cp.va ? 1 : 0, cp.tile_rows, cp.psplit,
+                lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials,
+                cp.n_rows, cp.n_tiles, cp.n_combs, cp.n_partials};
   hipError_t e =
       fw ? launch_plan_write(context_lens, query_start_loc, pp, workspace, lay, fw->k_new,
                              fw->v_new, fw->slots, total_q, k_cache, v_cache, p, stream)
@@ -606,33 +699,34 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
   if (e != hipSuccess) return hip_fail(e, "plan launch");
 
   AttnArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
-             max_blocks_per_seq, num_q_heads, total_q, scale * kLog2e, workspace, psplit};
+             max_blocks_per_seq, num_q_heads, total_q, scale * kLog2e, workspace, cp.psplit};
   // Optional events around one kernel, recorded on `stream` (profiling hook).
   const int timed = opt ? opt->timed_kernel : 0;
   auto mark = [&](int which, hipEvent_t ev) {
     if (timed == which && ev) (void)hipEventRecord(ev, stream);
   };
-  if (n_tiles > 0) {
+  if (cp.n_tiles > 0) {
     mark(PA_TIME_TILE, opt ? opt->timing_start : nullptr);
-    if ((e = launch_tile_attention(a, p, lay, (int)n_tiles, tile_rows, stream)) != hipSuccess)
+    if ((e = launch_tile_attention(a, p, lay, (int)cp.n_tiles, cp.tile_rows, stream)) != hipSuccess)
       return hip_fail(e, "multi-token attention launch");
     mark(PA_TIME_TILE, opt ? opt->timing_end : nullptr);
   }
-  if (n_rows > 0) {
+  if (cp.n_rows > 0) {
     mark(PA_TIME_ROWS, opt ? opt->timing_start : nullptr);
-    e = rows_on_mfma
-            ? launch_decode_mfma(a, p, lay, (int)n_rows, split,
+    e = cp.rows_on_mfma
+            ? launch_decode_mfma(a, p, lay, (int)cp.n_rows, cp.split,
                                  opt && (opt->flags & PA_FLAG_KV_UNSHARED), stream)
-            : launch_row_attention(a, p, lay, (int)n_rows, split, stream);
+            : launch_row_attention(a, p, lay, (int)cp.n_rows, cp.split, stream);
     if (e != hipSuccess) return hip_fail(e, "row attention launch");
     mark(PA_TIME_ROWS, opt ? opt->timing_end : nullptr);
   }
-  if (n_combs > 0) {
+  if (cp.n_combs > 0) {
     mark(PA_TIME_COMBINE, opt ? opt->timing_start : nullptr);
-    if ((e = launch_combine(a, p, lay, (int)n_combs, stream)) != hipSuccess)
+    if ((e = launch_combine(a, p, lay, (int)cp.n_combs, stream)) != hipSuccess)
       return hip_fail(e, "split combine launch");
     mark(PA_TIME_COMBINE, opt ? opt->timing_end : nullptr);
   }
+  if (validate_mode()) return read_status(workspace, stream);
   return PA_OK;
 }
 

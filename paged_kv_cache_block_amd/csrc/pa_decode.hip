@@ -115,7 +115,10 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs
   const int n = a.qsl[s + 1] - q0;
   const int L = a.context_lens[s];
   const int row = q0 + it.i;
-  if (row >= a.total_q) return;
+  if (row >= a.total_q) {
+    mark_dropped(a.ws, lay);
+    return;
+  }
   const int t0 = it.split * split_tokens;
   const int t1 = min(L - n + it.i + 1, t0 + split_tokens);
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
@@ -270,7 +273,10 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs
     }
   } else {
     const int64_t slot = it.pslot + it.split;
-    if (slot >= lay.cap_partials) return;
+    if (slot >= lay.cap_partials) {
+      mark_dropped(a.ws, lay);
+      return;
+    }
     float* po = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + lay.part_o) +
                 (slot * Hq + head) * D + 4 * grp;
 #pragma unroll

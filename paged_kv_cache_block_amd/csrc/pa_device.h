@@ -146,8 +146,14 @@ struct CombItem {
   int32_t nsplit;
   int32_t seq;
 };
+// Written by the planner at the start of every attention call.  `mismatch`
+// is nonzero when the work the device derives from context_lens /
+// query_start_loc differs from what the host derived from their mirrors (the
+// grids were sized from the latter); `dropped` is set by any kernel that had
+// to skip work because an index left the batch or the workspace.
 struct PlanCounts {
   int32_t rows, tiles, combs, partials;
+  int32_t mismatch, dropped;
 };
 
 }  // namespace pa

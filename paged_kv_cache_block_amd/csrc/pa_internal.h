@@ -48,7 +48,17 @@ struct PlanParams {
   int tile_rows;      // rows per MFMA multi-token work item
   int prefill_split;  // keys per split of a multi-token sequence (0: none)
   int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
+  // The counts the host derived from its mirrors (the launch sizes).
+  int64_t want_rows, want_tiles, want_combs, want_partials;
 };
+
+// A kernel that must skip work it was handed (an index outside the batch or
+// the workspace: the device batch disagrees with the host mirrors) records it
+// here for pa_attention_check.  Every writer stores the same value.
+__device__ __forceinline__ void mark_dropped(const void* ws, const WorkspaceLayout& lay) {
+  volatile int32_t* d = &reinterpret_cast<PlanCounts*>(static_cast<uint8_t*>(const_cast<void*>(ws)) + lay.counts)->dropped;
+  *d = 1;
+}
 
 hipError_t launch_write_kv(const void* k_new, const void* v_new, const int64_t* slots,
                            int num_tokens, void* k_cache, void* v_cache, const PoolArgs& p,

@@ -136,6 +136,9 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
     pc->tiles = (int32_t)min<int64_t>(scan[1][tid], pp.cap_tiles);
     pc->combs = (int32_t)min<int64_t>(scan[2][tid], pp.cap_combs);
     pc->partials = (int32_t)min<int64_t>(scan[3][tid], pp.cap_partials);
+    pc->mismatch = scan[0][tid] != pp.want_rows || scan[1][tid] != pp.want_tiles ||
+                   scan[2][tid] != pp.want_combs || scan[3][tid] != pp.want_partials;
+    pc->dropped = 0;
   }
 }
 

@@ -64,7 +64,10 @@ __global__ __launch_bounds__(64) void row_attn_kernel(AttnArgs a, PoolArgs p, Wo
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
   const int nb_max = p.num_blocks - 1;
   const int tb_max = a.max_blocks - 1;
-  if (row >= a.total_q) return;   // device batch disagrees with the host mirrors
+  if (row >= a.total_q) {          // device batch disagrees with the host mirrors
+    mark_dropped(a.ws, lay);
+    return;
+  }
 
   // Query slice of this lane, pre-scaled.
   float qv[GH][VEC];
@@ -194,7 +197,10 @@ __global__ __launch_bounds__(64) void row_attn_kernel(AttnArgs a, PoolArgs p, Wo
     float* po = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + lay.part_o);
     float2* pm = reinterpret_cast<float2*>(const_cast<uint8_t*>(ws) + lay.part_ml);
     const int64_t slot = it.pslot + it.split;
-    if (slot >= lay.cap_partials) return;
+    if (slot >= lay.cap_partials) {
+      mark_dropped(a.ws, lay);
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
 #pragma unroll
@@ -223,7 +229,11 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, WorkspaceLayou
   const int e = blockIdx.y * 256 + threadIdx.x;
   const int h = e / q4;
   const int d = (e - h * q4) * 4;
-  if (h >= Hq || ci.row >= a.total_q || ci.pslot < 0 || ci.pslot + ci.nsplit > lay.cap_partials) return;
+  if (h >= Hq) return;
+  if (ci.row >= a.total_q || ci.pslot < 0 || ci.pslot + ci.nsplit > lay.cap_partials) {
+    mark_dropped(a.ws, lay);
+    return;
+  }
   const float4* po = reinterpret_cast<const float4*>(
       reinterpret_cast<const float*>(ws + lay.part_o) + (int64_t)ci.pslot * Hq * D + h * D + d);
   const float2* pm = reinterpret_cast<const float2*>(ws + lay.part_ml) + (int64_t)ci.pslot * Hq + h;

@@ -148,6 +148,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   const int wr0 = r0 + 32 * wv;               // first row of the wave
   const int r = wr0 + col;
   const bool row_ok = r < R && q0 + r / G < a.total_q;
+  if (r < R && !row_ok) mark_dropped(a.ws, lay);   // rows past total_q: the batch disagrees
   const int qi = row_ok ? r / G : 0;
   const int hq = g * G + (row_ok ? r % G : 0);
   const int p_row = row_ok ? L - n + qi : -1;
@@ -437,7 +438,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   // in it); the combine kernel merges the splits.
   if (p_row < k0) return;
   const int64_t slot = (int64_t)ti.pslot + (int64_t)qi * key_splits(L, S) + ti.split;
-  if (slot >= lay.cap_partials) return;
+  if (slot >= lay.cap_partials) {
+    mark_dropped(a.ws, lay);
+    return;
+  }
   float* po = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + lay.part_o) + (slot * Hq + hq) * D;
 #pragma unroll
   for (int t = 0; t < NDT; ++t)

@@ -11,8 +11,15 @@
         copying a known byte count (bench.py --copy-calibration).  Prints a
         one-line traffic record for a profiles/*.md file.
 
-``traffic_record_for`` lets bench.py pick a record back up; a record only
-applies while the kernel's sources hash to the value stored in it.
+    python -m paged_kv_cache_block_amd.profiling mfma --kernel K --config C <db>
+        MFMA-busy fraction of kernel K from one --pmc run of
+        SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: the busy cycles summed
+        over the chip's SIMDs, over SIMDs x the launch's cycles per XCD.
+        Prints a one-line mfma record for a profiles/*.md file.
+
+``traffic_record_for`` / ``counter_record_for`` let bench.py pick a record
+back up; a record only applies while the kernel's sources hash to the value
+stored in it.
 """
 from __future__ import annotations
 
@@ -101,18 +108,38 @@ def traffic_record(kernel: str, config: int, fetch_db: str, write_db: str, copy_
             "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
 
 
-def traffic_record_for(kernel: str, config: int):
-    """The stored record for (kernel, config) if the kernel is unchanged since."""
+# MI355X: 256 compute units of 4 SIMDs, in 8 XCDs.
+NUM_SIMDS = 1024
+NUM_XCDS = 8
+
+
+def mfma_record(kernel: str, config: int, db: str) -> dict:
+    busy = _one(db, kernel, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _one(db, kernel, "GRBM_GUI_ACTIVE")
+    cycles = gui / NUM_XCDS
+    return {"kernel": kernel, "config": config, "source_sha256": kernel_source_hash(kernel),
+            "mfma_busy_frac": round(busy / (NUM_SIMDS * cycles), 4),
+            "mfma_busy_cycles": int(busy), "launch_cycles_per_xcd": int(cycles)}
+
+
+def counter_record_for(tag: str, kernel: str, config: int):
+    """The stored ``tag`` record for (kernel, config) if the kernel is
+    unchanged since it was taken."""
     want = kernel_source_hash(kernel)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as f:
             for line in f:
-                if line.startswith("traffic-record:"):
+                if line.startswith(tag + ":"):
                     rec = json.loads(line.split(":", 1)[1])
                     if rec.get("kernel") == kernel and rec.get("config") == config \
                             and rec.get("source_sha256") == want:
                         return rec
     return None
+
+
+def traffic_record_for(kernel: str, config: int):
+    """The stored traffic record for (kernel, config) if the kernel is unchanged since."""
+    return counter_record_for("traffic-record", kernel, config)
 
 
 def main(argv=None) -> int:
@@ -128,6 +155,10 @@ def main(argv=None) -> int:
     r.add_argument("--config", type=int, required=True)
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         r.add_argument("--" + k, required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--config", type=int, required=True)
+    m.add_argument("db")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace_table(a.db))
@@ -136,6 +167,8 @@ def main(argv=None) -> int:
             print(k)
             for c, v in sorted(cs.items()):
                 print(f"    {c:34s} {v:.6g}")
+    elif a.cmd == "mfma":
+        print("mfma-record: " + json.dumps(mfma_record(a.kernel, a.config, a.db)))
     else:
         rec = traffic_record(a.kernel, a.config, a.fetch, a.write, a.copy_fetch, a.copy_write)
         print("traffic-record: " + json.dumps(rec))

@@ -210,3 +210,116 @@ def test_empty_batch_is_ok_without_a_gpu(binding):
     st = b.LIB.pa_attention(None, None, None, None, ctypes.byref(desc), 4, None, 1, None, None,
                             S, 0, lh, qh, 0.125, None, 0, None, None)
     assert st == 0
+
+
+class _NoCalls:
+    """Stands in for the library: any entry point reached is a test failure."""
+    def __getattr__(self, name):
+        raise AssertionError(f"{name} was called with an argument on the wrong device")
+
+
+def test_binding_rejects_host_tensors_before_the_library(binding, monkeypatch):
+    """A CPU tensor where a device pointer is expected (or a device tensor
+    where the host pairs of a swap are expected) raises ValueError in the
+    binding, before any library call.  Pools on the 'meta' device stand in for
+    GPU tensors here: no memory is touched."""
+    import torch
+    monkeypatch.setattr(binding, "LIB", _NoCalls())
+    k = torch.empty((8, 2, 16, 64), dtype=torch.float16)
+    v = torch.empty((8, 2, 64, 16), dtype=torch.float16)
+    pairs = torch.zeros((2, 2), dtype=torch.int32)
+    slots = torch.zeros(3, dtype=torch.int64)
+    kn = torch.empty((3, 2, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="must be a tensor on"):
+        binding.pa_copy_blocks(k, v, pairs)
+    with pytest.raises(ValueError, match="must be a tensor on"):
+        binding.pa_write_kv(kn, kn.clone(), slots, k, v)
+    with pytest.raises(ValueError, match="must be a tensor on"):
+        binding.pa_copy_blocks_layers([k], [v], pairs)
+    with pytest.raises(ValueError, match="contiguous int32"):
+        binding.pa_copy_blocks(k, v, torch.zeros((2, 4), dtype=torch.int32)[:, ::2])
+    # a swap takes device pools and host pairs: device-side pairs are refused
+    mk = torch.empty((8, 2, 16, 64), dtype=torch.float16, device="meta")
+    mv = torch.empty((8, 2, 64, 16), dtype=torch.float16, device="meta")
+    with pytest.raises(ValueError, match="must be a"):
+        binding.pa_swap_blocks(mk, mv, k, v, pairs.to("meta"), binding.PA_SWAP_IN)
+    with pytest.raises(ValueError, match="must be a tensor on"):
+        binding.pa_swap_blocks(k, v, k, v, pairs, binding.PA_SWAP_IN)
+    lens = torch.tensor([5], dtype=torch.int32)
+    qsl = torch.tensor([0, 1], dtype=torch.int32)
+    q = torch.empty((1, 4, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="must be a tensor on"):
+        binding.pa_attention(q.clone(), q, k, v, torch.zeros((1, 1), dtype=torch.int32), lens, qsl,
+                             lens, qsl, 0.125, torch.empty(256, dtype=torch.uint8))
+
+
+def _adversarial_batches():
+    """Length mixes that stress the workspace bound: many long decodes, many
+    tiny prefills, one huge prefill, prefills whose causal ranges straddle
+    split boundaries, contexts of exactly the split length, empty sequences."""
+    import numpy as np
+    rng = np.random.default_rng(77)
+    yield "long decodes", [(4096, 1)] * 300
+    yield "tiny prefills", [(L, int(rng.integers(2, L + 1))) for L in rng.integers(2, 6, size=900)]
+    yield "one huge prefill", [(65_536, 8192)]
+    yield "huge prefill + decodes", [(60_000, 4000)] + [(30_000, 1)] * 40
+    yield "split boundaries", [(1024 * k + d, n) for k in (1, 2, 3) for d in (-1, 0, 1) for n in (1, 2, 129)]
+    yield "empties", [(int(L), 0) for L in rng.integers(1, 5000, size=64)] + [(5000, 1)]
+    for i in range(40):
+        S = int(rng.integers(1, 200))
+        seqs = []
+        for _ in range(S):
+            L = int(rng.choice([1, 2, 31, 32, 33, 1023, 1024, 1025, int(rng.integers(1, 20_000))]))
+            n = int(rng.choice([0, 1, 1, 2, min(L, int(rng.integers(1, 700))), L]))
+            seqs.append((L, min(n, L)))
+        yield f"random {i}", seqs
+
+
+@pytest.mark.parametrize("opt_kind", ["default", "split64", "psplit128", "psplit1024", "nosplit",
+                                      "tile256", "vector"])
+def test_workspace_bound_covers_every_plan(binding, opt_kind):
+    """For adversarial length mixes, a workspace of pa_attention_workspace_size
+    (num_seqs, total_q, max context) always holds the plan pa_attention makes
+    (host arithmetic only: pa_attention_plan touches no GPU)."""
+    import numpy as np
+    b = binding
+    opt = {"default": None, "split64": b.options(64), "psplit128": b.options(0, 128),
+           "psplit1024": b.options(0, 1024),
+           "nosplit": b.options(0, 0, b.PA_FLAG_NO_PREFILL_SPLIT),
+           "tile256": b.options(prefill_tile_rows=256),
+           "vector": b.options(0, 0, b.PA_FLAG_VECTOR_ALU)}[opt_kind]
+    for dtype, hq, hkv, bs in ((1, 40, 40, 32), (2, 64, 8, 16), (0, 8, 1, 8)):
+        desc = _desc(b, 1 << 20, bs, hkv, 128, dtype)
+        for name, seqs in _adversarial_batches():
+            lens = np.array([L for L, _ in seqs], dtype=np.int32)
+            qsl = np.concatenate([[0], np.cumsum([n for _, n in seqs])]).astype(np.int32)
+            mb = int(-(-lens.max() // bs))
+            ws = b.pa_attention_workspace_size(desc, hq, len(seqs), int(qsl[-1]), int(lens.max()), opt)
+            st, info = b.pa_attention_plan(desc, hq, mb, lens, qsl, ws, opt)
+            assert st == 0, (opt_kind, dtype, name, b.LIB.pa_last_error())
+            assert 0 < info.workspace_bytes <= ws, (name, info.workspace_bytes, ws)
+            # the same plan refuses a workspace one byte short of what it occupies
+            st2, info2 = b.pa_attention_plan(desc, hq, mb, lens, qsl, info.workspace_bytes - 1, opt)
+            if opt_kind in ("default", "split64", "tile256"):
+                # the automatic split may lengthen itself to fit, never fail silently
+                assert st2 in (0, -3) and (st2 == -3 or info2.workspace_bytes < info.workspace_bytes)
+            else:
+                assert st2 == -3, (opt_kind, name)
+
+
+def test_plan_counts_match_a_direct_count(binding):
+    """Decode rows split into ceil(keys / split) items; multi-token sequences
+    into ceil(n * G / tile_rows) tiles when not split."""
+    import numpy as np
+    b = binding
+    desc = _desc(b, 4096, 16, 4, 128, 1)
+    lens = np.array([100, 700, 64, 1000, 5], dtype=np.int32)
+    n = np.array([1, 1, 1, 300, 5])
+    qsl = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    opt = b.options(128, 0, b.PA_FLAG_NO_PREFILL_SPLIT, prefill_tile_rows=128)
+    st, info = b.pa_attention_plan(desc, 16, 64, lens, qsl, 1 << 30, opt)
+    assert st == 0
+    assert info.decode_split_tokens == 128 and info.prefill_split_tokens == 0
+    assert info.row_items == 1 + 6 + 1                     # ceil(100/128), ceil(700/128), ceil(64/128)
+    assert info.tile_items == -(-300 * 4 // 128) + -(-5 * 4 // 128)
+    assert info.combine_items == 1 and info.partial_slots == 6
