@@ -348,6 +348,37 @@ pa_status pa_write_kv_attention(void* out, const void* q, const void* k_new, con
                                 hipStream_t stream);
 
 /*
+ * pa_write_kv_attention_static -- pa_write_kv_attention without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The plan, split states and status live in a static device array of
+ * PA_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until
+ * the process ends.  The call allocates nothing: its first call on a device
+ * looks up that device's copy of the array, later calls reuse it.
+ *  Arguments, results, options and errors as for pa_write_kv_attention, with
+ *  the workspace replaced by the static scratch.  A batch whose plan needs
+ *  more than PA_STATIC_SCRATCH_BYTES (pa_attention_plan with that size
+ *  reports it) returns PA_ERR_WORKSPACE and enqueues nothing.  Under
+ *  PA_VALIDATE=1 only the final status check runs (the other checks copy
+ *  into host buffers).
+ *  Every call on one GPU shares that GPU's scratch, which keeps the last
+ *  call's contents (each call writes what it reads first, so nothing needs
+ *  clearing): calls that overlap on one GPU -- on two streams, or from two
+ *  host threads -- race and must be serialized by the caller.
+ */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_write_kv_attention_static(void* out, const void* q, const void* k_new,
+                                       const void* v_new, const int64_t* slot_mapping,
+                                       void* k_cache, void* v_cache, const pa_cache_desc* c,
+                                       int32_t num_q_heads, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       const int32_t* query_start_loc, int32_t num_seqs,
+                                       int32_t total_q, const int32_t* context_lens_host,
+                                       const int32_t* query_start_loc_host, float scale,
+                                       const pa_options* opt, hipStream_t stream);
+
+/*
  * pa_attention_check -- wait for `stream`, then report whether the last
  * pa_attention / pa_write_kv_attention call that used `workspace` ran every
  * work item it was sized for.

@@ -21,7 +21,8 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "P
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 SYMBOLS = ("pa_write_kv", "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks",
            "pa_attention_workspace_size", "pa_attention_plan", "pa_attention",
-           "pa_write_kv_attention", "pa_attention_check", "pa_last_error", "pa_version")
+           "pa_write_kv_attention", "pa_write_kv_attention_static", "pa_attention_check",
+           "pa_last_error", "pa_version")
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 MAX_LAYERS = 128
 
@@ -82,6 +83,10 @@ def _load() -> ctypes.CDLL:
                                           i32p, i32p, i32, i32, i32p, i32p, ctypes.c_float, vp,
                                           ctypes.c_size_t, opt_p, vp]
     lib.pa_write_kv_attention.restype = ctypes.c_int
+    lib.pa_write_kv_attention_static.argtypes = [vp, vp, vp, vp, i64p, vp, vp, desc_p, i32, i32p,
+                                                 i32, i32p, i32p, i32, i32, i32p, i32p,
+                                                 ctypes.c_float, opt_p, vp]
+    lib.pa_write_kv_attention_static.restype = ctypes.c_int
     lib.pa_attention_plan.argtypes = [desc_p, i32, i32, i32, i32, i32p, i32p, ctypes.c_size_t, opt_p,
                                       ctypes.POINTER(PaPlanInfo)]
     lib.pa_attention_plan.restype = ctypes.c_int
@@ -342,6 +347,37 @@ def pa_write_kv_attention(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, 
         _ptr(query_start_loc_host), float(scale), _ptr(workspace),
         0 if workspace is None else int(workspace.numel() * workspace.element_size()),
         ctypes.byref(opt) if opt is not None else None, _stream(stream)))
+
+
+def pa_write_kv_attention_static(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                 block_tables, context_lens, query_start_loc, context_lens_host,
+                                 query_start_loc_host, scale: float, opt: PaOptions | None = None,
+                                 stream=None) -> None:
+    """``pa_write_kv_attention`` with the library's static device scratch in
+    place of a workspace: the call allocates no device memory.  Calls that
+    overlap on one GPU share the scratch and must be serialized."""
+    desc = cache_desc(k_cache, v_cache)
+    tq, hq, s = _attention_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                query_start_loc, context_lens_host, query_start_loc_host, None)
+    if tuple(k_new.shape) != (tq, desc.num_kv_heads, desc.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [T_q][H_kv][D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("k_new/v_new must have the pool dtype")
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new/v_new must be contiguous")
+    if (slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous()
+            or slot_mapping.numel() != tq):
+        raise ValueError("slot_mapping must be a contiguous int64 [T_q] tensor")
+    _on_device(k_cache.device, k_new=k_new, v_new=v_new, slot_mapping=slot_mapping)
+    _check(LIB.pa_write_kv_attention_static(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
+        _ptr(v_cache), ctypes.byref(desc), hq, _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(context_lens), _ptr(query_start_loc), s, tq, _ptr(context_lens_host),
+        _ptr(query_start_loc_host), float(scale),
+        ctypes.byref(opt) if opt is not None else None, _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def version() -> int:

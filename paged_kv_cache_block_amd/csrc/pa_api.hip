@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -261,7 +262,8 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
                          const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
                          const int32_t* context_lens_host, const int32_t* query_start_loc_host,
                          float scale, void* workspace, size_t workspace_bytes,
-                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream);
+                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream,
+                         bool static_scratch);
 
 }  // namespace
 
@@ -481,7 +483,7 @@ pa_status pa_attention(void* out, const void* q, const void* k_cache, const void
                         num_q_heads, block_tables, max_blocks_per_seq, context_lens,
                         query_start_loc, num_seqs, total_q, context_lens_host,
                         query_start_loc_host, scale, workspace, workspace_bytes, opt, nullptr,
-                        stream);
+                        stream, false);
 }
 
 pa_status pa_write_kv_attention(void* out, const void* q, const void* k_new, const void* v_new,
@@ -498,7 +500,7 @@ pa_status pa_write_kv_attention(void* out, const void* q, const void* k_new, con
   return attention_impl(out, q, k_cache, v_cache, c, num_q_heads, block_tables,
                         max_blocks_per_seq, context_lens, query_start_loc, num_seqs, total_q,
                         context_lens_host, query_start_loc_host, scale, workspace,
-                        workspace_bytes, opt, &fw, stream);
+                        workspace_bytes, opt, &fw, stream, false);
 }
 
 }  // extern "C"
@@ -644,11 +646,16 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
                          const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
                          const int32_t* context_lens_host, const int32_t* query_start_loc_host,
                          float scale, void* workspace, size_t workspace_bytes,
-                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream) {
+                         const pa_options* opt, const FusedWrite* fw, hipStream_t stream,
+                         bool static_scratch) {
   CallPlan cp;
   pa_status st = plan_call(c, num_q_heads, max_blocks_per_seq, num_seqs, total_q,
                            context_lens_host, query_start_loc_host,
                            workspace ? workspace_bytes : 0, opt, &cp);
+  if (st == PA_ERR_WORKSPACE && total_q > 0 && static_scratch)
+    return fail(PA_ERR_WORKSPACE,
+                "the batch's plan needs %zu bytes of workspace; the static scratch holds %zu "
+                "(give pa_write_kv_attention a workspace instead)", cp.lay.total, workspace_bytes);
   if (st != PA_OK && !(st == PA_ERR_WORKSPACE && total_q == 0)) return st;
   if (total_q == 0) return PA_OK;
   const PoolArgs& p = cp.p;
@@ -665,7 +672,7 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
-  if (validate_mode()) {
+  if (validate_mode() && !static_scratch) {   // (these copies use host buffers)
     std::vector<int32_t> bt, lens, qsl;
     if ((st = fetch(bt, block_tables, (size_t)num_seqs * max_blocks_per_seq, stream)) != PA_OK) return st;
     if ((st = fetch(lens, context_lens, (size_t)num_seqs, stream)) != PA_OK) return st;
@@ -731,3 +738,57 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
 }
 
 }  // namespace
+
+// ---- the no-allocation entry point --------------------------------------
+// A file-scope device array serves as the workspace of
+// pa_write_kv_attention_static.  Host code never uses the array's name as an
+// address: on each device, with that device current, its address is looked up
+// once with hipGetSymbolAddress and kept.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+pa_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_write_kv_attention_static(
+    void* out, const void* q, const void* k_new, const void* v_new, const int64_t* slot_mapping,
+    void* k_cache, void* v_cache, const pa_cache_desc* c, int32_t num_q_heads,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* query_start_loc, int32_t num_seqs, int32_t total_q,
+    const int32_t* context_lens_host, const int32_t* query_start_loc_host, float scale,
+    const pa_options* opt, hipStream_t stream) {
+  static_assert(PA_STATIC_SCRATCH_BYTES == kScratchBytes, "scratch size of the ABI and the array");
+  void* ws = nullptr;
+  const pa_status st = scratch_of_current_device(&ws);
+  if (st != PA_OK) return st;
+  const FusedWrite fw{k_new, v_new, slot_mapping};
+  return attention_impl(out, q, k_cache, v_cache, c, num_q_heads, block_tables,
+                        max_blocks_per_seq, context_lens, query_start_loc, num_seqs, total_q,
+                        context_lens_host, query_start_loc_host, scale, ws, kScratchBytes, opt, &fw,
+                        stream, true);
+}
