@@ -50,7 +50,11 @@ struct PlanParams {
   int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
   // The counts the host derived from its mirrors (the launch sizes).
   int64_t want_rows, want_tiles, want_combs, want_partials;
+  // Multi-token items are listed longest first, bucketed by their key count
+  // >> lpt_shift (chosen so the longest context fits kLptBuckets buckets).
+  int lpt_shift;
 };
+constexpr int kLptBuckets = 512;
 
 // A kernel that must skip work it was handed (an index outside the batch or
 // the workspace: the device batch disagrees with the host mirrors) records it

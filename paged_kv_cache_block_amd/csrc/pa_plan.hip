@@ -17,6 +17,17 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kSplitList = 256;   // split multi-token sequences whose combine items are written by all threads
 
+// Keys of split k of a tile whose causal range ends at kend (split length S;
+// S = 0: the whole range).
+__device__ __forceinline__ int item_keys(int kend, int k, int S) {
+  return S > 0 ? min(kend, (k + 1) * S) - k * S : kend;
+}
+// Bucket of an item with `keys` keys: longer items get lower buckets.
+__device__ __forceinline__ int lpt_bucket(int keys, int shift) {
+  const int b = min(max(keys - 1, 0) >> shift, kLptBuckets - 1);
+  return kLptBuckets - 1 - b;
+}
+
 struct SplitSeq {
   int32_t seq, comb_base, pbase, i0, n, L, q0, ns;
 };
@@ -27,8 +38,11 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
   __shared__ int32_t scan[4][kPlanThreads];
   __shared__ SplitSeq split_list[kSplitList];
   __shared__ int32_t split_count;
+  __shared__ int32_t lpt_start[kLptBuckets];   // first list position of each bucket
+  __shared__ int32_t lpt_fill[kLptBuckets];    // items counted / placed per bucket
   const int tid = threadIdx.x;
   if (tid == 0) split_count = 0;
+  for (int b = tid; b < kLptBuckets; b += kPlanThreads) lpt_fill[b] = 0;
   const int S = pp.num_seqs;
   const int per = (S + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(S, tid * per);
@@ -67,6 +81,10 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
   int32_t base[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) base[k] = scan[k][tid] - c[k];
+  const int32_t part0 = base[3];   // this thread's first partial slot
+  int32_t total[4];                // the batch's counts (scan[0] is reused below)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) total[k] = scan[k][kPlanThreads - 1];
 
   RowItem* rows = reinterpret_cast<RowItem*>(ws + lay.rows);
   TileItem* tiles = reinterpret_cast<TileItem*>(ws + lay.tiles);
@@ -111,16 +129,60 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
       base[2] += tw.combs;
       base[3] += tw.slots;
     }
-    // Last tile first: later rows see the longest causal key range.
-    for (int t = w.tiles - 1; t >= 0; --t) {
-      const int nk = ns > 1 ? key_splits(tile_key_end(n, L, pp.group, pp.tile_rows, t), pp.prefill_split) : 1;
-      for (int k = 0; k < nk; ++k) {
-        if (base[1] < pp.cap_tiles) tiles[base[1]] = TileItem{s, t, k, pbase};
-        base[1] += 1;
-      }
+    // Histogram of the sequence's tile items by key count (longest first).
+    for (int t = 0; t < w.tiles; ++t) {
+      const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
+      const int nk = ns > 1 ? key_splits(kend, pp.prefill_split) : 1;
+      for (int k = 0; k < nk; ++k)
+        atomicAdd(&lpt_fill[lpt_bucket(item_keys(kend, k, ns > 1 ? pp.prefill_split : 0), pp.lpt_shift)], 1);
     }
   }
   __syncthreads();
+  // Bucket starts: an exclusive scan of the histogram (two buckets a thread).
+  static_assert(kLptBuckets == 2 * kPlanThreads, "two buckets per planner thread");
+  {
+    const int b0 = lpt_fill[2 * tid], b1 = lpt_fill[2 * tid + 1];
+    __syncthreads();
+    scan[0][tid] = b0 + b1;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const int v = tid >= off ? scan[0][tid - off] : 0;
+      __syncthreads();
+      scan[0][tid] += v;
+      __syncthreads();
+    }
+    const int ex = scan[0][tid] - b0 - b1;
+    lpt_start[2 * tid] = ex;
+    lpt_start[2 * tid + 1] = ex + b0;
+    lpt_fill[2 * tid] = 0;
+    lpt_fill[2 * tid + 1] = 0;
+  }
+  __syncthreads();
+  // Place every tile item at its bucket's next free position.  The order
+  // inside a bucket is arbitrary: each item computes outputs of its own.
+  int32_t part = part0;   // partial slots handed out as in the first pass
+  for (int s = s0; s < s1; ++s) {
+    const int n = qsl[s + 1] - qsl[s];
+    const int L = lens[s];
+    const SeqWork w = seq_work(n, pp.vector_all, pp.group, pp.tile_rows);
+    for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
+      const int nr = row_splits(L - n + i + 1, pp.split_tokens);
+      if (nr > 1) part += nr;
+    }
+    if (w.tiles == 0) continue;
+    const int ns = key_splits(L, pp.prefill_split);
+    const int32_t pbase = ns > 1 ? part : -1;
+    if (ns > 1) part += tile_work(n, L, pp.group, pp.tile_rows, w.tiles, pp.prefill_split).slots;
+    for (int t = 0; t < w.tiles; ++t) {
+      const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
+      const int nk = ns > 1 ? key_splits(kend, pp.prefill_split) : 1;
+      for (int k = 0; k < nk; ++k) {
+        const int b = lpt_bucket(item_keys(kend, k, ns > 1 ? pp.prefill_split : 0), pp.lpt_shift);
+        const int at = lpt_start[b] + atomicAdd(&lpt_fill[b], 1);
+        if (at < pp.cap_tiles) tiles[at] = TileItem{s, t, k, pbase};
+      }
+    }
+  }
   const int nl = min(split_count, kSplitList);
   for (int e = 0; e < nl; ++e) {
     const SplitSeq q = split_list[e];
@@ -132,12 +194,12 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
   }
   if (tid == kPlanThreads - 1) {
     PlanCounts* pc = reinterpret_cast<PlanCounts*>(ws + lay.counts);
-    pc->rows = (int32_t)min<int64_t>(scan[0][tid], pp.cap_rows);
-    pc->tiles = (int32_t)min<int64_t>(scan[1][tid], pp.cap_tiles);
-    pc->combs = (int32_t)min<int64_t>(scan[2][tid], pp.cap_combs);
-    pc->partials = (int32_t)min<int64_t>(scan[3][tid], pp.cap_partials);
-    pc->mismatch = scan[0][tid] != pp.want_rows || scan[1][tid] != pp.want_tiles ||
-                   scan[2][tid] != pp.want_combs || scan[3][tid] != pp.want_partials;
+    pc->rows = (int32_t)min<int64_t>(total[0], pp.cap_rows);
+    pc->tiles = (int32_t)min<int64_t>(total[1], pp.cap_tiles);
+    pc->combs = (int32_t)min<int64_t>(total[2], pp.cap_combs);
+    pc->partials = (int32_t)min<int64_t>(total[3], pp.cap_partials);
+    pc->mismatch = total[0] != pp.want_rows || total[1] != pp.want_tiles ||
+                   total[2] != pp.want_combs || total[3] != pp.want_partials;
     pc->dropped = 0;
   }
 }

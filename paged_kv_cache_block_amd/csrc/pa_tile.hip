@@ -27,8 +27,8 @@
 // The running max is only raised (and O rescaled) when a row's max grows by
 // more than 2^8, so most iterations skip the rescale.  The LDS operands of a
 // half are read before its softmax, so their latency hides behind it.
-// Workgroups are numbered so that the tiles sharing one (sequence, KV head)
-// run on one XCD and reuse its L2.
+// Work items come longest first from the plan, and workgroups are numbered
+// so that each XCD gets an even share of them (see the item mapping below).
 
 #include "pa_internal.h"
 
@@ -120,9 +120,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
   const PlanCounts* pc = reinterpret_cast<const PlanCounts*>(ws + lay.counts);
   const int Hkv = p.num_kv_heads;
-  const int logical = xcd_order(blockIdx.x, gridDim.x);
-  const int g = logical / num_tiles;
-  const int item = logical - g * num_tiles;
+  // The plan lists work items longest first.  With a multiple of 8 KV heads,
+  // each XCD takes whole heads (their lists are alike, so the XCDs' shares
+  // are too), so that the tiles sharing one (sequence, head) meet in its L2,
+  // and runs them item-major over its heads: its workgroups start in list
+  // order, longest first.  (The dispatcher hands workgroup b to XCD b % 8.)
+  // Otherwise the list goes round-robin over the XCDs, item by item, so that
+  // each gets long and short items.
+  int g, item;
+  if (Hkv % 8 == 0) {
+    const int hpx = Hkv >> 3;                  // KV heads per XCD
+    const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+    item = pos / hpx;
+    g = xcd * hpx + (pos - item * hpx);
+  } else {
+    item = blockIdx.x / Hkv;
+    g = blockIdx.x - item * Hkv;
+  }
   if (item >= pc->tiles) return;
   const TileItem ti = reinterpret_cast<const TileItem*>(ws + lay.tiles)[item];
 
