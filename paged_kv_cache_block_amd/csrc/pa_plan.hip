@@ -129,18 +129,28 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
       base[2] += tw.combs;
       base[3] += tw.slots;
     }
-    // Histogram of the sequence's tile items by key count (longest first).
-    for (int t = 0; t < w.tiles; ++t) {
-      const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
-      const int nk = ns > 1 ? key_splits(kend, pp.prefill_split) : 1;
-      for (int k = 0; k < nk; ++k)
-        atomicAdd(&lpt_fill[lpt_bucket(item_keys(kend, k, ns > 1 ? pp.prefill_split : 0), pp.lpt_shift)], 1);
+    // Items are listed longest first.  A sequence whose keys are not split
+    // goes in as one contiguous run (its tiles re-read the same K/V, which
+    // then meet in one L2), placed by its longest item (the last tile); the
+    // items of a split sequence go in one by one (those of one key split read
+    // the same keys and have the same length, so they stay together).
+    if (ns > 1) {
+      for (int t = 0; t < w.tiles; ++t) {
+        const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
+        const int nk = key_splits(kend, pp.prefill_split);
+        for (int k = 0; k < nk; ++k)
+          atomicAdd(&lpt_fill[lpt_bucket(item_keys(kend, k, pp.prefill_split), pp.lpt_shift)], 1);
+      }
+    } else {
+      atomicAdd(&lpt_fill[lpt_bucket(tile_key_end(n, L, pp.group, pp.tile_rows, w.tiles - 1), pp.lpt_shift)],
+                w.tiles);
     }
   }
   __syncthreads();
   // Bucket starts: an exclusive scan of the histogram (two buckets a thread).
+  // (A batch without multi-token items skips this and the placement.)
   static_assert(kLptBuckets == 2 * kPlanThreads, "two buckets per planner thread");
-  {
+  if (total[1] > 0) {
     const int b0 = lpt_fill[2 * tid], b1 = lpt_fill[2 * tid + 1];
     __syncthreads();
     scan[0][tid] = b0 + b1;
@@ -156,12 +166,12 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
     lpt_start[2 * tid + 1] = ex + b0;
     lpt_fill[2 * tid] = 0;
     lpt_fill[2 * tid + 1] = 0;
+    __syncthreads();
   }
-  __syncthreads();
-  // Place every tile item at its bucket's next free position.  The order
-  // inside a bucket is arbitrary: each item computes outputs of its own.
+  // Place every item (or run) at its bucket's next free position.  The
+  // order inside a bucket is arbitrary: each item computes outputs of its own.
   int32_t part = part0;   // partial slots handed out as in the first pass
-  for (int s = s0; s < s1; ++s) {
+  for (int s = s0; s < s1 && total[1] > 0; ++s) {
     const int n = qsl[s + 1] - qsl[s];
     const int L = lens[s];
     const SeqWork w = seq_work(n, pp.vector_all, pp.group, pp.tile_rows);
@@ -172,15 +182,23 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
     if (w.tiles == 0) continue;
     const int ns = key_splits(L, pp.prefill_split);
     const int32_t pbase = ns > 1 ? part : -1;
-    if (ns > 1) part += tile_work(n, L, pp.group, pp.tile_rows, w.tiles, pp.prefill_split).slots;
-    for (int t = 0; t < w.tiles; ++t) {
-      const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
-      const int nk = ns > 1 ? key_splits(kend, pp.prefill_split) : 1;
-      for (int k = 0; k < nk; ++k) {
-        const int b = lpt_bucket(item_keys(kend, k, ns > 1 ? pp.prefill_split : 0), pp.lpt_shift);
-        const int at = lpt_start[b] + atomicAdd(&lpt_fill[b], 1);
-        if (at < pp.cap_tiles) tiles[at] = TileItem{s, t, k, pbase};
+    if (ns > 1) {
+      part += tile_work(n, L, pp.group, pp.tile_rows, w.tiles, pp.prefill_split).slots;
+      for (int t = 0; t < w.tiles; ++t) {
+        const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
+        const int nk = key_splits(kend, pp.prefill_split);
+        for (int k = 0; k < nk; ++k) {
+          const int b = lpt_bucket(item_keys(kend, k, pp.prefill_split), pp.lpt_shift);
+          const int at = lpt_start[b] + atomicAdd(&lpt_fill[b], 1);
+          if (at < pp.cap_tiles) tiles[at] = TileItem{s, t, k, pbase};
+        }
       }
+    } else {
+      // The run, last tile (the most keys) first.
+      const int b = lpt_bucket(tile_key_end(n, L, pp.group, pp.tile_rows, w.tiles - 1), pp.lpt_shift);
+      int at = lpt_start[b] + atomicAdd(&lpt_fill[b], w.tiles);
+      for (int t = w.tiles - 1; t >= 0; --t, ++at)
+        if (at < pp.cap_tiles) tiles[at] = TileItem{s, t, 0, pbase};
     }
   }
   const int nl = min(split_count, kSplitList);

@@ -35,8 +35,9 @@ import sqlite3
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {
-    "decode_mfma_kernel": ["csrc/pa_decode.hip"],
-    "tile_attn_kernel": ["csrc/pa_tile.hip"],
+    # The planner's order of work items shapes the attention kernels' traffic.
+    "decode_mfma_kernel": ["csrc/pa_decode.hip", "csrc/pa_plan.hip"],
+    "tile_attn_kernel": ["csrc/pa_tile.hip", "csrc/pa_plan.hip"],
     "row_attn_kernel": ["csrc/pa_rows.hip"],
     "combine_kernel": ["csrc/pa_rows.hip"],
     "write_kv_kernel": ["csrc/pa_kv.hip"],
