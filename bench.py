@@ -524,6 +524,19 @@ def swap(args) -> int:
           "attention_per_layer_ms": round(_time_ms(db.attention, reps), 4),
           "swaps_then_attention_ms": round(_time_ms(serial, reps), 4),
           "layerwise_pipeline_ms": round(_time_ms(pipelined, reps), 4)})
+    # Release what the swaps used while the runtime is fully up: wait for the
+    # copy streams, drop the pipeline (streams, events) and the pinned host
+    # pools, and return torch's cached pinned blocks, so that none of it is
+    # left for the interpreter's exit.
+    torch.cuda.synchronize()
+    for st in (pipe.copy_stream, pipe.out_stream, s1, s2):
+        st.synchronize()
+    del plan, pipe, hkl, hvl, pin, pout, s1, s2, db
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch._C._host_emptyCache()
     return 0
 
 
