@@ -152,10 +152,26 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs
   __shared__ __attribute__((aligned(16))) u32x4 kl[32 * CPRW];
   const int pkey = lane / CPRW, pchunk = lane % CPRW;
 
+  // The split's block ids, one per lane, 64 blocks at a time (clamped to the
+  // table row and the pool, so every load below stays inside them): a step
+  // takes its ids with readlane, so its K/V loads wait on no table load.
+  // The split starts on an even block (split_tokens is a multiple of 64), so
+  // the two 16-token blocks of a step never straddle two windows.
+  const int blk0 = t0 / BS;
+  int win = -1;
+  unsigned btlane = 0;
+  auto block_id = [&](int b) -> unsigned {   // b: block of the sequence, wave-uniform
+    const int w = (b - blk0) >> 6;
+    if (w != win) {
+      win = w;
+      btlane = min((unsigned)bt[min(blk0 + 64 * w + lane, tb_max)], nb_max);
+    }
+    return (unsigned)__builtin_amdgcn_readlane((int)btlane, b - blk0 - 64 * w);
+  };
   auto load = [&](int c0, Stage<D>& st) {
-    const unsigned b0 = min((unsigned)bt[min(c0 / BS, tb_max)], nb_max);
+    const unsigned b0 = block_id(c0 / BS);
     unsigned b1 = b0;
-    if constexpr (BS == 16) b1 = min((unsigned)bt[min(c0 / BS + 1, tb_max)], nb_max);
+    if constexpr (BS == 16) b1 = block_id(c0 / BS + 1);
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       const int kk = KPI * i + pkey;                      // 0..31
