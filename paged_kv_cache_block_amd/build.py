@@ -27,6 +27,11 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas", "-munsafe-fp-atomics"]
+# Per-source extra flags.  The multi-token kernel's inner loop (LDS operand
+# reads, MFMAs, softmax) runs about 1.5% faster on the long mixed batch when
+# the machine scheduler favours instruction-level parallelism over occupancy
+# (it is register-bound at two waves per SIMD either way).
+SOURCE_FLAGS = {"pa_tile.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def hipcc() -> str:
@@ -42,7 +47,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> tuple[str, float, str]:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEVICE_FLAGS
+    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEVICE_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), [])
     t = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True)
     # The host pass does not know the device-only feature name and says so.

@@ -43,7 +43,8 @@ KERNEL_SOURCES = {
     "write_kv_kernel": ["csrc/pa_kv.hip"],
     "copy_blocks_kernel": ["csrc/pa_kv.hip"],
 }
-COMMON_SOURCES = ["csrc/pa_device.h", "csrc/pa_internal.h"]
+# build.py holds the compile flags (per source, too).
+COMMON_SOURCES = ["csrc/pa_device.h", "csrc/pa_internal.h", "build.py"]
 COPY_CAL_BYTES = 2 * 4096 * 40 * 16 * 128 * 2      # bench.py --copy-calibration, each way
 
 
