@@ -135,11 +135,12 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
     // items of a split sequence go in one by one (those of one key split read
     // the same keys and have the same length, so they stay together).
     if (ns > 1) {
+      // Every split of a tile but its last holds exactly prefill_split keys.
       for (int t = 0; t < w.tiles; ++t) {
         const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
         const int nk = key_splits(kend, pp.prefill_split);
-        for (int k = 0; k < nk; ++k)
-          atomicAdd(&lpt_fill[lpt_bucket(item_keys(kend, k, pp.prefill_split), pp.lpt_shift)], 1);
+        if (nk > 1) atomicAdd(&lpt_fill[lpt_bucket(pp.prefill_split, pp.lpt_shift)], nk - 1);
+        atomicAdd(&lpt_fill[lpt_bucket(item_keys(kend, nk - 1, pp.prefill_split), pp.lpt_shift)], 1);
       }
     } else {
       atomicAdd(&lpt_fill[lpt_bucket(tile_key_end(n, L, pp.group, pp.tile_rows, w.tiles - 1), pp.lpt_shift)],
@@ -187,11 +188,16 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
       for (int t = 0; t < w.tiles; ++t) {
         const int kend = tile_key_end(n, L, pp.group, pp.tile_rows, t);
         const int nk = key_splits(kend, pp.prefill_split);
-        for (int k = 0; k < nk; ++k) {
-          const int b = lpt_bucket(item_keys(kend, k, pp.prefill_split), pp.lpt_shift);
-          const int at = lpt_start[b] + atomicAdd(&lpt_fill[b], 1);
-          if (at < pp.cap_tiles) tiles[at] = TileItem{s, t, k, pbase};
+        // The full splits as one run of a bucket, then the last split.
+        if (nk > 1) {
+          const int b = lpt_bucket(pp.prefill_split, pp.lpt_shift);
+          const int at = lpt_start[b] + atomicAdd(&lpt_fill[b], nk - 1);
+          for (int k = 0; k < nk - 1; ++k)
+            if (at + k < pp.cap_tiles) tiles[at + k] = TileItem{s, t, k, pbase};
         }
+        const int b = lpt_bucket(item_keys(kend, nk - 1, pp.prefill_split), pp.lpt_shift);
+        const int at = lpt_start[b] + atomicAdd(&lpt_fill[b], 1);
+        if (at < pp.cap_tiles) tiles[at] = TileItem{s, t, nk - 1, pbase};
       }
     } else {
       // The run, last tile (the most keys) first.
