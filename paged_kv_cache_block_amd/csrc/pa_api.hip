@@ -95,7 +95,13 @@ int prefill_split(const pa_options* opt) {
 // batch's items fill the workgroup slots once (two pieces are always
 // allowed).  The floor is kMinAutoPrefillSplit, or kMinAutoPrefillSplitSparse
 // when the unsplit items fill less than a quarter of the slots (then
-// parallelism outweighs the partial states).
+// parallelism outweighs the partial states).  When the unsplit items fill
+// every slot already, nothing is split either while the longest item is
+// under twice a slot's fair share W / P: the planner lists items longest
+// first, so such an item starts first and ends within the launch's length
+// (on the unified fp16 batch, 640 items over 512 slots with a longest item
+// of 1.5 shares, splitting gained nothing and cost 36 MB of partial-state
+// writes).
 constexpr int kMinAutoPrefillSplit = 1024;
 constexpr int kMinAutoPrefillSplitSparse = 256;
 
@@ -135,6 +141,7 @@ int choose_prefill_split(const int32_t* lens, const int32_t* qsl, int num_seqs, 
   }
   if (work == 0) return 0;
   const int64_t slots = (int64_t)cu_count() * (tile_rows == kTileRowsWide ? 1 : 2);
+  if (items * num_kv_heads >= slots && (int64_t)longest * slots < 2 * work * num_kv_heads) return 0;
   const bool sparse = items * num_kv_heads * 4 < slots;
   const int64_t want = std::max<int64_t>(work * num_kv_heads / (2 * slots),
                                          sparse ? kMinAutoPrefillSplitSparse : kMinAutoPrefillSplit);
