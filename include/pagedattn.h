@@ -101,8 +101,11 @@ typedef struct {
    * Bit 1 (PA_FLAG_KV_UNSHARED): the caller asserts that no physical block
    * is read by two sequences of this call (no reference-count sharing, no
    * sub-requests over one table row).  Decode then streams K/V with
-   * non-temporal loads, which is faster when nothing is re-read and slower
-   * when blocks are shared; results are identical either way.
+   * non-temporal loads, and its work items are listed longest first and
+   * dealt round-robin over the XCDs (each XCD's L2 then serves an even share
+   * of the work instead of the neighbouring rows that would share blocks);
+   * faster when nothing is re-read, slower when blocks are shared; results
+   * are identical either way.
    * Bit 2 (PA_FLAG_NO_PREFILL_SPLIT): with prefill_split_tokens = 0, never
    * split multi-token contexts.
    * Other bits must be 0. */

@@ -228,6 +228,10 @@ struct CallPlan {
   PoolArgs p;
   int group = 0, max_len = 0, split = 0, tile_rows = kTileRows, psplit = 0;
   bool va = false, rows_on_mfma = false;
+  // Row items listed longest first and dealt round-robin over the XCDs (each
+  // gets an even share of the work).  Only where no block is read by two
+  // sequences: sharers of a prompt then no longer meet in one L2.
+  bool rows_dealt = false;
   int64_t n_rows = 0, n_tiles = 0, n_combs = 0, n_partials = 0;
   WorkspaceLayout lay{};
 };
@@ -623,9 +627,11 @@ pa_status plan_call(const pa_cache_desc* c, int32_t num_q_heads, int32_t max_blo
     fits = count();
   }
   cp->psplit = psplit;
-  if (cp->n_rows > 0x7fffffff || cp->n_tiles > 0x7fffffff || cp->n_partials > 0x7fffffff)
+  if (cp->n_rows > 0x7fffffff || cp->n_tiles > 0x7fffffff || cp->n_partials > 0x7fffffff ||
+      decode_mfma_groups(cp->n_rows, p.num_kv_heads, true) > 0x7fffffff)
     return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
   cp->rows_on_mfma = !va && decode_mfma_supported(p, group);
+  cp->rows_dealt = cp->rows_on_mfma && opt && (opt->flags & PA_FLAG_KV_UNSHARED);
   if (cp->n_rows > 0 && !cp->rows_on_mfma && p.block_size > 64)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d needs the fp16/bf16 MFMA kernels", p.block_size);
   if (!fits)
@@ -706,7 +712,7 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
   int lpt_shift = 0;   // buckets of 2^lpt_shift keys, the longest context in the last
   while (((cp.max_len - 1) >> lpt_shift) >= kLptBuckets) ++lpt_shift;
   PlanParams pp{num_seqs, cp.split, cp.group, cp.va ? 1 : 0, cp.tile_rows, cp.psplit,
-                lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials,
+                cp.rows_dealt ? 1 : 0, lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials,
                 cp.n_rows, cp.n_tiles, cp.n_combs, cp.n_partials, lpt_shift};
   hipError_t e =
       fw ? launch_plan_write(context_lens, query_start_loc, pp, workspace, lay, fw->k_new,
@@ -715,7 +721,8 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
   if (e != hipSuccess) return hip_fail(e, "plan launch");
 
   AttnArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
-             max_blocks_per_seq, num_q_heads, total_q, scale * kLog2e, workspace, cp.psplit};
+             max_blocks_per_seq, num_q_heads, total_q, scale * kLog2e, workspace, cp.psplit,
+             cp.rows_dealt ? 1 : 0};
   // Optional events around one kernel, recorded on `stream` (profiling hook).
   const int timed = opt ? opt->timed_kernel : 0;
   auto mark = [&](int which, hipEvent_t ev) {

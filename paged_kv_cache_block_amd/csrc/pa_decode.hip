@@ -98,10 +98,22 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs
   // so that consecutive items -- the splits of one row, and rows of adjacent
   // sequences, which share prompt blocks when a block manager forks them --
   // run on one XCD.
+  // With a.rows_dealt the plan lists items longest first and they are dealt
+  // round-robin over the XCDs instead, whole items (all KV heads) at a time:
+  // XCD x takes items x, x + 8, x + 16, ..., so each gets an even share of
+  // the work (used when no block is read by two rows).
   const int Hkv = p.num_kv_heads;
-  const int logical = xcd_order(blockIdx.x, gridDim.x);
-  const int item = logical / Hkv;
-  const int g = logical - item * Hkv;
+  int item, g;
+  if (a.rows_dealt) {
+    const int pos = blockIdx.x >> 3;
+    const int round = pos / Hkv;
+    g = pos - round * Hkv;
+    item = 8 * round + (blockIdx.x & 7);
+  } else {
+    const int logical = xcd_order(blockIdx.x, gridDim.x);
+    item = logical / Hkv;
+    g = logical - item * Hkv;
+  }
   if (item >= pc->rows) return;
   const RowItem it = reinterpret_cast<const RowItem*>(ws + lay.rows)[item];
 
@@ -308,8 +320,9 @@ __global__ __launch_bounds__(64, 2) void decode_mfma_kernel(AttnArgs a, PoolArgs
 template <int DT, int D, bool NT>
 hipError_t launch_d(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay, int items,
                     int split, hipStream_t s) {
-  if ((int64_t)items * p.num_kv_heads > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(items * p.num_kv_heads);
+  const int64_t groups = decode_mfma_groups(items, p.num_kv_heads, a.rows_dealt != 0);
+  if (groups > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)groups);
   if (p.block_size == 16)
     hipLaunchKernelGGL((decode_mfma_kernel<DT, D, 16, NT>), grid, dim3(64), 0, s, a, p, lay, split);
   else if (p.block_size == 32)
@@ -331,6 +344,10 @@ hipError_t launch_nt(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout
 }
 
 }  // namespace
+
+int64_t decode_mfma_groups(int64_t num_items, int num_kv_heads, bool dealt) {
+  return (dealt ? (num_items + 7) / 8 * 8 : num_items) * num_kv_heads;
+}
 
 bool decode_mfma_supported(const PoolArgs& p, int group) {
   return (p.dtype == DT_F16 || p.dtype == DT_BF16) && (p.block_size == 16 || p.block_size == 32 || p.block_size == 64 || p.block_size == 128) &&

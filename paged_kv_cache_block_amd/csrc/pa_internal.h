@@ -47,6 +47,7 @@ struct PlanParams {
   int vector_all;     // 1: every row goes to the row kernel
   int tile_rows;      // rows per MFMA multi-token work item
   int prefill_split;  // keys per split of a multi-token sequence (0: none)
+  int rows_dealt;     // 1: list row items longest first, for dealing over the XCDs
   int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
   // The counts the host derived from its mirrors (the launch sizes).
   int64_t want_rows, want_tiles, want_combs, want_partials;
@@ -55,6 +56,8 @@ struct PlanParams {
   int lpt_shift;
 };
 constexpr int kLptBuckets = 512;
+// Row items listed longest first go in this many buckets of split length.
+constexpr int kRowBuckets = 64;
 
 // A kernel that must skip work it was handed (an index outside the batch or
 // the workspace: the device batch disagrees with the host mirrors) records it
@@ -110,6 +113,7 @@ struct AttnArgs {
   float scale_log2;   // scale * log2(e)
   void* ws;
   int prefill_split;  // keys per split of a multi-token sequence (0: none)
+  int rows_dealt;     // 1: row items are listed longest first and dealt over the XCDs
 };
 
 hipError_t launch_row_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
@@ -117,6 +121,9 @@ hipError_t launch_row_attention(const AttnArgs& a, const PoolArgs& p, const Work
 bool decode_mfma_supported(const PoolArgs& p, int group);
 hipError_t launch_decode_mfma(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                               int num_items, int split_tokens, bool stream_kv, hipStream_t s);
+// Workgroups of the decode kernel's grid: one per (row item, KV head), or,
+// with row items dealt over the XCDs, whole rounds of 8 items.
+int64_t decode_mfma_groups(int64_t num_items, int num_kv_heads, bool dealt);
 hipError_t launch_combine(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,
                           int num_combs, hipStream_t s);
 hipError_t launch_tile_attention(const AttnArgs& a, const PoolArgs& p, const WorkspaceLayout& lay,

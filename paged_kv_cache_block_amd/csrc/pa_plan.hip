@@ -28,6 +28,12 @@ __device__ __forceinline__ int lpt_bucket(int keys, int shift) {
   return kLptBuckets - 1 - b;
 }
 
+// Bucket of a row item with `keys` of a `split`-key split: full splits in
+// bucket 0, shorter ones later (longest first).
+__device__ __forceinline__ int row_bucket(int keys, int split) {
+  return (int)((int64_t)(split - keys) * (kRowBuckets - 1) / split);
+}
+
 struct SplitSeq {
   int32_t seq, comb_base, pbase, i0, n, L, q0, ns;
 };
@@ -40,9 +46,13 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
   __shared__ int32_t split_count;
   __shared__ int32_t lpt_start[kLptBuckets];   // first list position of each bucket
   __shared__ int32_t lpt_fill[kLptBuckets];    // items counted / placed per bucket
+  __shared__ int32_t row_start[kRowBuckets];   // the same for row items listed longest first
+  __shared__ int32_t row_fill[kRowBuckets];
   const int tid = threadIdx.x;
   if (tid == 0) split_count = 0;
   for (int b = tid; b < kLptBuckets; b += kPlanThreads) lpt_fill[b] = 0;
+  for (int b = tid; b < kRowBuckets; b += kPlanThreads) row_fill[b] = 0;
+  __syncthreads();   // (row_fill is counted in the first pass)
   const int S = pp.num_seqs;
   const int per = (S + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(S, tid * per);
@@ -54,11 +64,16 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
     const int L = lens[s];
     const SeqWork w = seq_work(n, pp.vector_all, pp.group, pp.tile_rows);
     for (int i = w.row_first; i < w.row_first + w.rows; ++i) {
-      const int ns = row_splits(L - n + i + 1, pp.split_tokens);
+      const int keys = L - n + i + 1;
+      const int ns = row_splits(keys, pp.split_tokens);
       c[0] += ns;
       if (ns > 1) {
         c[2] += 1;
         c[3] += ns;
+      }
+      if (pp.rows_dealt) {
+        if (ns > 1) atomicAdd(&row_fill[0], ns - 1);
+        atomicAdd(&row_fill[row_bucket(keys - (ns - 1) * pp.split_tokens, pp.split_tokens)], 1);
       }
     }
     const TileWork tw = tile_work(n, L, pp.group, pp.tile_rows, w.tiles, pp.prefill_split);
@@ -78,6 +93,15 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
     for (int k = 0; k < 4; ++k) scan[k][tid] += v[k];
     __syncthreads();
   }
+  if (pp.rows_dealt && tid == 0) {   // bucket starts of the row items (the scan's syncs ordered the counts)
+    int at = 0;
+    for (int b = 0; b < kRowBuckets; ++b) {
+      row_start[b] = at;
+      at += row_fill[b];
+      row_fill[b] = 0;
+    }
+  }
+  if (pp.rows_dealt) __syncthreads();
   int32_t base[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) base[k] = scan[k][tid] - c[k];
@@ -102,9 +126,23 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
         base[2] += 1;
         base[3] += ns;
       }
-      for (int k = 0; k < ns; ++k) {
-        if (base[0] < pp.cap_rows) rows[base[0]] = RowItem{s, i, k, pslot};
-        base[0] += 1;
+      if (pp.rows_dealt) {
+        // Longest first: the full splits as one run of bucket 0, the last
+        // split in its length's bucket.
+        const int keys = L - n + i + 1;
+        if (ns > 1) {
+          const int at = row_start[0] + atomicAdd(&row_fill[0], ns - 1);
+          for (int k = 0; k < ns - 1; ++k)
+            if (at + k < pp.cap_rows) rows[at + k] = RowItem{s, i, k, pslot};
+        }
+        const int b = row_bucket(keys - (ns - 1) * pp.split_tokens, pp.split_tokens);
+        const int at = row_start[b] + atomicAdd(&row_fill[b], 1);
+        if (at < pp.cap_rows) rows[at] = RowItem{s, i, ns - 1, pslot};
+      } else {
+        for (int k = 0; k < ns; ++k) {
+          if (base[0] < pp.cap_rows) rows[base[0]] = RowItem{s, i, k, pslot};
+          base[0] += 1;
+        }
       }
     }
     if (w.tiles == 0) continue;

@@ -442,14 +442,16 @@ def test_graph_capture_replays(torch_cuda, cfg):
         assert np.array_equal(got, want), f"replay {r}"
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
-def test_streaming_hint_is_bit_identical(torch_cuda, cfg):
-    """The no-sharing hint only changes the cache policy of the loads."""
+@pytest.mark.parametrize("cfg,split", [(2, 0), (3, 0), (5, 0), (2, 64), (3, 64)])
+def test_streaming_hint_is_bit_identical(torch_cuda, cfg, split):
+    """The no-sharing hint changes the cache policy of the decode loads and
+    the order of the decode work (listed longest first, dealt over the XCDs);
+    neither changes a bit of the output."""
     from paged_kv_cache_block_amd import binding
     w = small_workload(cfg)
-    say("stream hint", w.name)
-    a = run_gpu(w).out_numpy()
-    b = run_gpu(w, binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED)).out_numpy()
+    say("stream hint", w.name, "split", split)
+    a = run_gpu(w, binding.options(split)).out_numpy()
+    b = run_gpu(w, binding.options(split, 0, binding.PA_FLAG_KV_UNSHARED)).out_numpy()
     assert np.array_equal(bits(a), bits(b))
 
 
