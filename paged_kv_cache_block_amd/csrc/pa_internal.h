@@ -28,7 +28,10 @@ constexpr int kAutoTargetWaves = 8192;
 // MFMA tile), so no tile straddles two splits.
 constexpr int kPrefillSplitQuantum = 128;
 constexpr int kMinAutoSplit = 64;
-constexpr int kMaxAutoSplit = 1024;
+// (The cap matters for large GQA batches: the long mixed bf16 batch's 128
+// decode rows take 1472-key splits, 4.6% faster than 1024 once its row items
+// are dealt evenly over the XCDs.)
+constexpr int kMaxAutoSplit = 2048;
 
 struct PoolArgs {
   int num_blocks, block_size, num_kv_heads, head_dim, dtype;
