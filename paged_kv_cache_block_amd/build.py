@@ -31,7 +31,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 # reads, MFMAs, softmax) runs about 1.5% faster on the long mixed batch when
 # the machine scheduler favours instruction-level parallelism over occupancy
 # (it is register-bound at two waves per SIMD either way).
-SOURCE_FLAGS = {"pa_tile.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# The planner's LDS atomics (bucket counts and places) are left to the LDS:
+# the compiler's atomic optimizer would turn each into a loop over the active
+# lanes of the wave, which made the planner of a 64-row decode batch take
+# 8.5 us instead of about 5.
+SOURCE_FLAGS = {"pa_tile.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+                "pa_plan.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:

@@ -711,8 +711,10 @@ pa_status attention_impl(void* out, const void* q, void* k_cache, void* v_cache,
   const WorkspaceLayout& lay = cp.lay;
   int lpt_shift = 0;   // buckets of 2^lpt_shift keys, the longest context in the last
   while (((cp.max_len - 1) >> lpt_shift) >= kLptBuckets) ++lpt_shift;
+  int row_shift = 0;   // (split - 1) >> row_shift < kRowBuckets
+  while (((cp.split - 1) >> row_shift) >= kRowBuckets) ++row_shift;
   PlanParams pp{num_seqs, cp.split, cp.group, cp.va ? 1 : 0, cp.tile_rows, cp.psplit,
-                cp.rows_dealt ? 1 : 0, lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials,
+                cp.rows_dealt ? 1 : 0, row_shift, lay.cap_rows, lay.cap_tiles, lay.cap_combs, lay.cap_partials,
                 cp.n_rows, cp.n_tiles, cp.n_combs, cp.n_partials, lpt_shift};
   hipError_t e =
       fw ? launch_plan_write(context_lens, query_start_loc, pp, workspace, lay, fw->k_new,

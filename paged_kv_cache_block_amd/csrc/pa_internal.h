@@ -51,6 +51,7 @@ struct PlanParams {
   int tile_rows;      // rows per MFMA multi-token work item
   int prefill_split;  // keys per split of a multi-token sequence (0: none)
   int rows_dealt;     // 1: list row items longest first, for dealing over the XCDs
+  int row_shift;      // row items' length buckets: (split - keys) >> row_shift
   int64_t cap_rows, cap_tiles, cap_combs, cap_partials;
   // The counts the host derived from its mirrors (the launch sizes).
   int64_t want_rows, want_tiles, want_combs, want_partials;

@@ -28,10 +28,11 @@ __device__ __forceinline__ int lpt_bucket(int keys, int shift) {
   return kLptBuckets - 1 - b;
 }
 
-// Bucket of a row item with `keys` of a `split`-key split: full splits in
-// bucket 0, shorter ones later (longest first).
-__device__ __forceinline__ int row_bucket(int keys, int split) {
-  return (int)((int64_t)(split - keys) * (kRowBuckets - 1) / split);
+// Bucket of a row item with `keys` (1..split) of a `split`-key split: full
+// splits in bucket 0, shorter ones later (longest first); `shift` makes
+// (split - 1) >> shift < kRowBuckets.
+__device__ __forceinline__ int row_bucket(int keys, int split, int shift) {
+  return (split - keys) >> shift;
 }
 
 struct SplitSeq {
@@ -73,7 +74,7 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
       }
       if (pp.rows_dealt) {
         if (ns > 1) atomicAdd(&row_fill[0], ns - 1);
-        atomicAdd(&row_fill[row_bucket(keys - (ns - 1) * pp.split_tokens, pp.split_tokens)], 1);
+        atomicAdd(&row_fill[row_bucket(keys - (ns - 1) * pp.split_tokens, pp.split_tokens, pp.row_shift)], 1);
       }
     }
     const TileWork tw = tile_work(n, L, pp.group, pp.tile_rows, w.tiles, pp.prefill_split);
@@ -93,15 +94,23 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
     for (int k = 0; k < 4; ++k) scan[k][tid] += v[k];
     __syncthreads();
   }
-  if (pp.rows_dealt && tid == 0) {   // bucket starts of the row items (the scan's syncs ordered the counts)
-    int at = 0;
-    for (int b = 0; b < kRowBuckets; ++b) {
-      row_start[b] = at;
-      at += row_fill[b];
-      row_fill[b] = 0;
+  if (pp.rows_dealt) {
+    // Bucket starts of the row items: an exclusive scan by the first wave, one
+    // bucket a lane (the scan above ordered the counts).
+    static_assert(kRowBuckets == 64, "one wave scans the row buckets");
+    if (tid < kRowBuckets) {
+      const int cnt = row_fill[tid];
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (tid >= off) incl += v;
+      }
+      row_start[tid] = incl - cnt;
+      row_fill[tid] = 0;
     }
+    __syncthreads();
   }
-  if (pp.rows_dealt) __syncthreads();
   int32_t base[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) base[k] = scan[k][tid] - c[k];
@@ -135,7 +144,7 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens,
           for (int k = 0; k < ns - 1; ++k)
             if (at + k < pp.cap_rows) rows[at + k] = RowItem{s, i, k, pslot};
         }
-        const int b = row_bucket(keys - (ns - 1) * pp.split_tokens, pp.split_tokens);
+        const int b = row_bucket(keys - (ns - 1) * pp.split_tokens, pp.split_tokens, pp.row_shift);
         const int at = row_start[b] + atomicAdd(&row_fill[b], 1);
         if (at < pp.cap_rows) rows[at] = RowItem{s, i, ns - 1, pslot};
       } else {
