@@ -588,6 +588,8 @@ def main(argv=None) -> int:
                     help="also time the dominant kernel with L2 and MALL flushed before each step")
     ap.add_argument("--separate-write", action="store_true",
                     help="time pa_write_kv then pa_attention instead of pa_write_kv_attention")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed (launch gaps out)")
     ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 128, 256],
                     help="rows per multi-token MFMA work item (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -730,6 +732,29 @@ def main(argv=None) -> int:
         dom_cold_ms = float(np.mean([a.elapsed_time(b) for a, b in evs3]))
         del scratch
 
+    # --graph: the same step captured once in a HIP graph and replayed K
+    # times, back to back.  The replay has the same kernels and work; what it
+    # removes is the host's per-launch cost and the gaps between launches,
+    # which is what a launch-bound step (few, short kernels) spends beyond its
+    # kernels.  Reported beside the eager step, never as `value`.
+    graph_ms = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_step(base_opt)
+        torch.cuda.synchronize()
+        for _ in range(max(args.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(K):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+        del g
+
     value = model["step_bytes"] / (ms_step * 1e-3) / 1e9
     rows_kernel = ("decode_mfma_kernel" if w.dtype != "f32" and w.block_size in (16, 32)
                    else "row_attn_kernel")
@@ -817,6 +842,9 @@ def main(argv=None) -> int:
         "roofline": roof,
         **others,
         "kernels_ms": {k2: round(v, 5) for k2, v in per_kernel.items()},
+        **({"graph_replay": {"ms_per_step": round(graph_ms, 5),
+                             "note": "the same step captured once in a HIP graph and replayed"}}
+           if graph_ms is not None else {}),
         "derived": extra,
         "cpu_baseline": cpu,
     }
