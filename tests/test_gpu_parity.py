@@ -455,6 +455,44 @@ def test_streaming_hint_is_bit_identical(torch_cuda, cfg, split):
     assert np.array_equal(bits(a), bits(b))
 
 
+@pytest.mark.parametrize("cfg,split", [(2, 0), (2, 64), (3, 0), (5, 0)])
+def test_dealt_row_list_is_longest_first(torch_cuda, cfg, split):
+    """With the no-sharing hint the planner lists the decode work longest
+    first: every full split, then the last splits in buckets of descending
+    length.  White-box: reads the row list the plan leaves in the workspace
+    (16-byte records (seq, row, split, first partial slot) right after the
+    256-byte status block) and checks it is exactly the expected set of
+    splits, in that order."""
+    torch = torch_cuda
+    from paged_kv_cache_block_amd import binding
+    w = config_workload(cfg)
+    opt = binding.options(split, 0, binding.PA_FLAG_KV_UNSHARED)
+    db = run_gpu(w, opt, fused=True)
+    desc = binding.cache_desc(db.k_cache, db.v_cache)
+    st, info = binding.pa_attention_plan(desc, w.num_q_heads, w.block_tables.shape[1],
+                                         w.context_lens, w.query_start_loc,
+                                         db.workspace.numel(), opt)
+    assert st == 0
+    S = info.decode_split_tokens
+    n_items = int(info.row_items)
+    torch.cuda.synchronize()
+    raw = db.workspace[256:256 + 16 * n_items].cpu().numpy().view(np.int32).reshape(-1, 4)
+    n_new = np.diff(w.query_start_loc)
+    want = set()
+    for s_ in np.flatnonzero(n_new == 1):
+        L = int(w.context_lens[s_])
+        for k in range(-(-L // S)):
+            want.add((int(s_), 0, k))
+    got = [(int(a), int(b), int(c)) for a, b, c, _ in raw]
+    assert len(got) == len(want) and set(got) == want
+    shift = 0
+    while (S - 1) >> shift >= 64:
+        shift += 1
+    keys = [min(int(w.context_lens[a]), (c + 1) * S) - c * S for a, _, c in got]
+    buckets = [(S - k) >> shift for k in keys]
+    assert buckets == sorted(buckets), "row items not listed longest first"
+
+
 def test_split_lengths_agree(torch_cuda):
     from paged_kv_cache_block_amd import binding
     w = small_workload(5)
