@@ -103,13 +103,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void tile_attn_kernel(AttnArgs a, 
   // contiguous 512-byte runs (one base address per lane plus an immediate).
   // Run r of K is (32-key half u, k-step ks, lane half hh) with
   // r = 2 (u KS + ks) + hh; run r of V^T is (u, head-dim tile t, k-step v2,
-  // hh) with r = 4 (u NDT + t) + 2 v2 + hh.  The run pitch carries p extra
-  // slots, chosen so that the 16 lanes of each quarter-wave tile store hit 16
-  // distinct 16-byte bank groups: the 16 chunks of one key (p = 1) or two
-  // keys (p = 2) for K, and 4 head-dim rows x 4 key chunks for V (p = 4).
-  // Reads are 16 consecutive slots per quarter wave, conflict-free as well.
-  constexpr int KRUN = 8 * (32 + (D == 128 ? 1 : 2));   // K run pitch (elements)
-  constexpr int VRUN = 8 * (32 + 4);                    // V^T run pitch (elements)
+  // hh) with r = 4 (u NDT + t) + 2 v2 + hh.  The LDS takes a 16-byte store 8
+  // lanes at a time into a 128-byte window of banks (the bank-conflict counter
+  // shows it: pitches that spread 16 lanes over 256 bytes left the V stores
+  // 2-way conflicted), so the run pitch carries p extra slots that send each
+  // 8-lane group of a tile store to 8 distinct 16-byte bank groups: K lanes
+  // hold 8 chunks of one key row (pitch = 16 bytes mod 128: p = 1), V lanes 4
+  // key chunks x 2 head-dim rows (pitch = 32 bytes mod 128: p = 2).  Reads
+  // are 16 consecutive slots per quarter wave, conflict-free with any pitch.
+  constexpr int KRUN = 8 * (32 + 1);   // K run pitch (elements)
+  constexpr int VRUN = 8 * (32 + 2);   // V^T run pitch (elements)
   constexpr int KSTAGE = 2 * NH * KS * KRUN;
   constexpr int VSTAGE = 4 * NH * NDT * VRUN;
   constexpr int TROWS = 32 * NW;    // rows per workgroup
