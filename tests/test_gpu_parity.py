@@ -608,7 +608,7 @@ def _random_batch_spec(seed):
             h, n = int(rng.integers(1, 300)), 0
         seqs.append((h, n, 2 if h >= 2 * bs and rng.random() < 0.3 else 1))
     mode = str(rng.choice(["default", "split64", "psplit128", "nopsplit", "tile128", "tile256",
-                           "rows", "stream"]))
+                           "rows", "stream", "stream64"]))
     if bs == 128 and mode == "rows":     # 128-token blocks have no vector-ALU path
         mode = "default"
     nblocks = 2 * sum(-(-(h + n) // bs) for h, n, _ in seqs) + 64
@@ -627,7 +627,8 @@ def test_random_batches(torch_cuda, seed):
            "tile128": binding.options(prefill_tile_rows=128),
            "tile256": binding.options(prefill_tile_rows=256),
            "rows": binding.options(0, 0, binding.PA_FLAG_VECTOR_ALU),
-           "stream": binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED)}[mode]
+           "stream": binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED),
+           "stream64": binding.options(64, 0, binding.PA_FLAG_KV_UNSHARED)}[mode]
     w = build_batch(f"random {seed}", dtype, hkv * g, hkv, d, bs, nblocks, seqs, seed)
     say("random", seed, dtype, "D", d, "bs", bs, "H", hkv * g, "/", hkv, "seqs", seqs, mode)
     db = run_gpu(w, opt)
