@@ -36,20 +36,24 @@ def _static_call(binding, db, out):
                                          db.context_lens_host, db.qsl_host, db.w.scale, db.opt)
 
 
-def test_static_scratch_matches_the_workspace_entry_point():
+@pytest.mark.parametrize("hint", [False, True], ids=["default", "kv_unshared"])
+def test_static_scratch_matches_the_workspace_entry_point(hint):
+    """With the no-sharing hint the plan also lists the decode work longest
+    first (for dealing over the XCDs), in the same static scratch."""
     import torch
     assert torch.cuda.is_available()
     from paged_kv_cache_block_amd import binding
     from paged_kv_cache_block_amd.step import DeviceBatch
+    opt = binding.options(0, 0, binding.PA_FLAG_KV_UNSHARED) if hint else None
     big = small_workload(5)           # multi-token and decode rows, split decode contexts
     small = small_workload(3)         # a smaller batch on the second call
     for i, w in enumerate((big, small)):
-        print(f"[case] static scratch call {i}: {w.name}", flush=True)
-        ref = DeviceBatch(w)
+        print(f"[case] static scratch call {i} (hint {hint}): {w.name}", flush=True)
+        ref = DeviceBatch(w, opt=opt)
         ref.write_history()
         ref.copy_blocks()
         ref.write_attention()
-        st = DeviceBatch(w)
+        st = DeviceBatch(w, opt=opt)
         st.write_history()
         st.copy_blocks()
         out = torch.empty_like(st.q)
